@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-2 streaming-state hot path on one MI355X.
+
+One bench step is one pass of every path over one batch of synthetic input:
+  decode   256 slots x (H=128, P=64, N=128) fp32 state, one token each, seeded
+           per-slot resets (p = 0.02)                                  [headline]
+  replay   ReplaySSM verify of 5 in-flight tokens (real + 4 drafts, p = 0.7)
+           per slot, window 16, then commit
+  copy     the copy-state-per-draft baseline of the same verify, then commit
+  prefill  one 65,536-token chunk of 8 packed bf16 sequences (H=128, P=64,
+           N=128), resets at sequence starts, final states as checkpoints
+Each path is timed with events on the stream it runs on; ``value`` is the
+decode state bandwidth (algorithmic state + input + output bytes per step
+divided by the decode kernel time).  Replay windows 8 and 32, the
+Mamba-130M-shaped chunked streaming layer and the CPU oracle are measured
+beside the steps.  Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MIB = 1 << 20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", default="", help="comma list of decode,replay,copy,prefill (profiling)")
+    ap.add_argument("--skip-extras", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """Events around launches on the current stream; mean of the recorded pairs."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path shards by batch or head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from streaming_state_amd import inputs
+    from streaming_state_amd import ssm
+    only = set(filter(None, args.only.split(",")))
+    want = (lambda k: not only or k in only)
+    K, Wm = args.steps, args.warmup
+    dev = "cuda"
+
+    # ------------------------------------------------------------ decode setup
+    w2 = inputs.W2
+    Bd, H, P, N, G = w2["batch"], w2["H"], w2["P"], w2["N"], w2["G"]
+    A2, D2 = inputs.params(2, H)
+    dec = ssm.StreamState(H, P, N, Bd, torch.from_numpy(A2).to(dev),
+                          torch.from_numpy(D2).to(dev), G=G)
+    dec.init(np.arange(Bd), inputs.device_state(2, Bd, H, P, N))
+    dec_slots = inputs.slot_permutation(2, Bd, Bd)
+    n_dec_inputs = w2["steps"]
+    dec_in = [inputs.device_tokens(2, Bd, H, P, N, G, seed_extra=s) for s in range(n_dec_inputs)]
+    dec_reset = [inputs.device_resets(2, s, Bd) for s in range(n_dec_inputs)]
+    state_b = H * P * N * 4
+
+    def dec_bytes(reset):
+        nr = int(reset.sum())
+        st = (Bd - nr) * state_b + Bd * state_b
+        io = Bd * (H * P * 4 * 2 + H * 4 + 2 * G * N * 4)
+        return st + io, st
+
+    # ------------------------------------------------------------ replay setup
+    w3 = inputs.W3
+    n_in = w3["T"] + 1
+    A3, D3 = inputs.params(3, H)
+    acc_all = inputs.acceptances(w3["steps"], Bd, T=w3["T"], p=w3["p"])
+    spec_in = []
+    for s in range(8):
+        x, dt, B, C = inputs.device_tokens(3, Bd * n_in, H, P, N, G, seed_extra=s)
+        spec_in.append((x.view(Bd, n_in, H, P), dt.view(Bd, n_in, H), B.view(Bd, n_in, G, N),
+                        C.view(Bd, n_in, G, N)))
+    init3 = inputs.device_state(3, Bd, H, P, N)
+
+    def make_replay(W):
+        r = ssm.StreamState(H, P, N, Bd, torch.from_numpy(A3).to(dev),
+                            torch.from_numpy(D3).to(dev), G=G)
+        r.init(np.arange(Bd), init3)
+        r.replay_attach(W)
+        return r
+
+    rep16 = make_replay(16) if want("replay") else None
+    cop = None
+    if want("copy"):
+        cop = ssm.StreamState(H, P, N, Bd, torch.from_numpy(A3).to(dev),
+                              torch.from_numpy(D3).to(dev), G=G)
+        cop.init(np.arange(Bd), init3)
+        cop.copy_attach(n_in)
+    slots3 = np.arange(Bd, dtype=np.int32)
+
+    # ----------------------------------------------------------- prefill setup
+    w4 = inputs.W4
+    L4 = w4["L"]
+    pre = None
+    if want("prefill"):
+        d4 = inputs.device_prefill(L4, H, P, N, G)
+        lengths = inputs.sequence_lengths()
+        reset4, cu4, ends4 = inputs.packed_layout(lengths)
+        pre = ssm.StreamState(H, P, N, 1, d4["A"], d4["D"], G=G, io_dtype="bf16")
+        pre.reset([0])
+        y4 = torch.empty((L4, H, P), dtype=torch.bfloat16, device=dev)
+        ck4 = torch.empty((len(ends4), H, P, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("setup done")
+
+    t_dec, t_rep, t_cop, t_pre = (Timer(torch) for _ in range(4))
+    y_dec = torch.empty((Bd, H, P), dtype=torch.float32, device=dev)
+    y_spec = torch.empty((Bd, n_in, H, P), dtype=torch.float32, device=dev)
+    step_bytes, step_state_bytes = [], []
+    pre_seq = [0]
+    flushes_before = 0
+
+    def one_step(s, timed):
+        i = s % n_dec_inputs
+        if want("decode"):
+            e = t_dec.start() if timed else None
+            dec.decode_step(dec_slots, *dec_in[i], reset=dec_reset[i], y=y_dec)
+            if timed:
+                t_dec.stop(e)
+                b, sb = dec_bytes(dec_reset[i])
+                step_bytes.append(b)
+                step_state_bytes.append(sb)
+        a = acc_all[s % len(acc_all)]
+        sp = spec_in[s % len(spec_in)]
+        if rep16 is not None:
+            e = t_rep.start() if timed else None
+            rep16.replay_step(slots3, *sp, y=y_spec)
+            if timed:
+                t_rep.stop(e)
+            rep16.replay_commit(slots3, a)
+        if cop is not None:
+            e = t_cop.start() if timed else None
+            cop.copy_step(slots3, *sp, y=y_spec)
+            if timed:
+                t_cop.stop(e)
+            cop.copy_commit(slots3, a)
+        if pre is not None:
+            e = t_pre.start() if timed else None
+            pre.scan_chunk(0, pre_seq[0], d4["x"], d4["dt"], d4["B"], d4["C"], y=y4,
+                           reset=reset4, ckpt_at=ends4, ckpt_out=ck4)
+            pre_seq[0] += 1
+            if timed:
+                t_pre.stop(e)
+
+    for s in range(Wm):
+        one_step(s, False)
+    torch.cuda.synchronize()
+    log(f"warmup {Wm} done")
+    if rep16 is not None:
+        flushes_before = rep16.counters()["replay_flushes"]
+    t0 = time.perf_counter()
+    for s in range(Wm, Wm + K):
+        one_step(s, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {K} steps in {wall:.3f} s")
+
+    out = {}
+    comp = {}
+    if want("decode"):
+        ms = np.array(t_dec.ms())
+        gbps = np.array(step_bytes) / (ms * 1e-3) / 1e9
+        state_gbps = np.array(step_state_bytes) / (ms * 1e-3) / 1e9
+        comp["decode"] = dict(ms_mean=float(ms.mean()), ms_median=float(np.median(ms)),
+                              GBps=float(gbps.mean()), state_GBps=float(state_gbps.mean()),
+                              frac_hbm=float(gbps.mean() / HBM_PEAK_GBPS),
+                              bytes_per_step=float(np.mean(step_bytes)))
+    if rep16 is not None:
+        ms = np.array(t_rep.ms())
+        comp["replay_W16"] = dict(ms_mean=float(ms.mean()), ms_median=float(np.median(ms)),
+                                  flushes=int(rep16.counters()["replay_flushes"] - flushes_before))
+    if cop is not None:
+        ms = np.array(t_cop.ms())
+        cbytes = Bd * state_b * (1 + n_in) + Bd * n_in * (H * P * 8 + H * 4 + 2 * G * N * 4)
+        comp["copy"] = dict(ms_mean=float(ms.mean()), ms_median=float(np.median(ms)),
+                            GBps=float(cbytes / (ms.mean() * 1e-3) / 1e9))
+        if rep16 is not None:
+            comp["replay_vs_copy_speedup_W16"] = comp["copy"]["ms_mean"] / comp["replay_W16"]["ms_mean"]
+    if pre is not None:
+        ms = np.array(t_pre.ms())
+        comp["prefill"] = dict(ms_mean=float(ms.mean()), tokens_per_s=float(L4 / (ms.mean() * 1e-3)),
+                               algorithmic_GFLOP=415.1)
+        comp["prefill"]["TFLOPs_algorithmic"] = 415.1e9 / (ms.mean() * 1e-3) / 1e12
+
+    # ------------------------------------------------------------- extras
+    extras = {}
+    if not args.skip_extras and not only:
+        # replay at W = 8 and 32 against the same copy baseline
+        for W in (8, 32):
+            r = make_replay(W)
+            tm = Timer(torch)
+            nst = 48
+            for s in range(nst + 4):
+                sp = spec_in[s % len(spec_in)]
+                e = tm.start() if s >= 4 else None
+                r.replay_step(slots3, *sp, y=y_spec)
+                if s >= 4:
+                    tm.stop(e)
+                r.replay_commit(slots3, acc_all[s])
+            torch.cuda.synchronize()
+            ms = float(np.mean(tm.ms()))
+            extras[f"replay_W{W}"] = dict(ms_mean=ms, flushes=r.counters()["replay_flushes"],
+                                          steps=nst + 4)
+            if cop is not None:
+                extras[f"replay_vs_copy_speedup_W{W}"] = comp["copy"]["ms_mean"] / ms
+            r.destroy()
+            del r
+        # Mamba-130M-shaped streaming layer: chunk sizes 1, 17, 64, 256 and full
+        w1 = inputs.W1
+        L1, H1 = w1["L"], w1["H"]
+        A1, D1 = inputs.params(1, H1)
+        x1, dt1, B1, C1 = inputs.device_tokens(1, L1, H1, P, N, G, seed_extra=0)
+        s1 = ssm.StreamState(H1, P, N, 1, torch.from_numpy(A1).to(dev),
+                             torch.from_numpy(D1).to(dev), G=G)
+        stream1 = {}
+        for chunk in (L1, 256, 64, 17, 1):
+            s1.reset([0])
+            sizes = [chunk] * (L1 // chunk) + ([L1 % chunk] if L1 % chunk else [])
+            for rep in range(2):  # the first run warms caches
+                s1.reset([0])
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                tw = time.perf_counter()
+                e0.record()
+                t = 0
+                for q, sz in enumerate(sizes):
+                    s1.scan_chunk(0, q, x1[t:t + sz], dt1[t:t + sz], B1[t:t + sz], C1[t:t + sz])
+                    t += sz
+                e1.record()
+                torch.cuda.synchronize()
+                wall1 = time.perf_counter() - tw
+            gpu_ms = e0.elapsed_time(e1)
+            stream1[str(chunk)] = dict(calls=len(sizes), tokens_per_s=L1 / (gpu_ms * 1e-3),
+                                       us_per_call=gpu_ms * 1e3 / len(sizes),
+                                       host_wall_us_per_call=wall1 * 1e6 / len(sizes))
+        extras["stream_130m"] = stream1
+        # plain device copy of 1 GiB for the achievable-bandwidth context
+        a = torch.empty(256 * MIB, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        for _ in range(10):
+            e = tm.start()
+            b.copy_(a)
+            tm.stop(e)
+        torch.cuda.synchronize()
+        extras["torch_copy_1GiB_GBps"] = 2 * a.numel() * 4 / (np.mean(tm.ms()) * 1e-3) / 1e9
+        del a, b
+
+    # --------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline and want("decode"):
+        cpu = cpu_baseline(inputs, dec_in, dec_reset, A2, D2, Bd, H, P, N, G, args.cpu_seconds,
+                           torch)
+
+    dec_c = comp.get("decode", {})
+    total_ms = sum(v["ms_mean"] for k, v in comp.items() if isinstance(v, dict) and "ms_mean" in v)
+    line = {
+        "metric": "decode state GB/s (% of HBM peak) at B=256; prefill tokens/s; replay vs copy speedup",
+        "value": round(dec_c.get("GBps", 0.0), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode B=256 H=128 P=64 N=128 fp32 state, reset p=0.02; "
+                               "replay/copy verify n_in=5 W=16; prefill 65536 tokens bf16",
+                   "batch": Bd, "H": H, "P": P, "N": N, "prefill_tokens": L4},
+        "components": comp,
+        "frac_of_hbm_peak": round(dec_c.get("frac_hbm", 0.0), 4),
+        "prefill_tokens_per_s": comp.get("prefill", {}).get("tokens_per_s"),
+        "replay_vs_copy_speedup": {"W16": comp.get("replay_vs_copy_speedup_W16"),
+                                   "W8": extras.get("replay_vs_copy_speedup_W8"),
+                                   "W32": extras.get("replay_vs_copy_speedup_W32")},
+        "sum_of_path_ms": round(total_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(dec_c.get("GBps", 0.0), 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_c.get("GBps", 0.0) / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "decode_kernel<float>",
+                     "algorithmic_bytes_per_launch": dec_c.get("bytes_per_step")},
+        "cpu_baseline": cpu,
+        "extras": extras,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inputs, dec_in, dec_reset, A, D, Bd, H, P, N, G, seconds, torch):
+    """The fp64 oracle's decode on host cores over whole decode steps of the same
+    workload (all 256 slots, all heads), as many as fit in ``seconds``."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    state = np.zeros((Bd, H, P, N))
+    pos = np.zeros(Bd, np.int64)
+    slots = np.arange(Bd, dtype=np.int32)
+    done, bytes_, t_used = 0, 0.0, 0.0
+    while t_used < seconds and done < len(dec_in):
+        x, dt, B, C = (t.cpu().numpy() for t in dec_in[done])
+        reset = dec_reset[done]
+        t0 = time.perf_counter()
+        oracle.decode(state, pos, slots, x, dt, B, C, A, D, reset=reset, n_threads=cores)
+        t_used += time.perf_counter() - t0
+        nr = int(reset.sum())
+        bytes_ += (Bd - nr) * H * P * N * 4 + Bd * H * P * N * 4 + \
+            Bd * (H * P * 8 + H * 4 + 2 * G * N * 4)
+        done += 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(bytes_ / t_used / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} full decode steps (256 slots x 128 heads, fp64) in {t_used:.1f} s; "
+                      f"fp32-equivalent state bytes; {model}; {platform.machine()}"}
+
+
+if __name__ == "__main__":
+    main()

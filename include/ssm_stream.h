@@ -1,0 +1,283 @@
+/*
+ * ssm_stream.h -- C ABI of the MI355X (gfx950) Mamba-2 streaming-state library.
+ *
+ * The library advances the Mamba-2 selective-scan recurrence, per head h of a
+ * layer with H heads, head dim P, state size N and G groups of B/C
+ * (g = h / (H/G)):
+ *
+ *     h_t = exp(dt_t[h] * A[h]) * h_{t-1} + dt_t[h] * x_t[h,:] (outer) B_t[g,:]
+ *     y_t[h,p] = sum_n h_t[p,n] * C_t[g,n] + D[h] * x_t[h,p]
+ *
+ * ("decay the old state, then add the new token's contribution": "Why
+ * Speculative Decoding Slows Hybrid Mamba Models at Large Batch Sizes",
+ * section "The Fix: Log the Inputs, Checkpoint the State"; the matrix and
+ * recurrent views of the same algebra: "Mamba Streaming State That Survives
+ * Chunking", section "Separate Mamba-2 algebra from kernel behavior").
+ *
+ * Three paths advance it, all on the caller's HIP stream:
+ *   ssm_scan_chunk   a chunk of L tokens of one stream, with carry-in/out,
+ *                    per-token reset flags and mid-chunk checkpoints;
+ *   ssm_decode_step  one token for each of a batch of streams (slots);
+ *   ssm_replay_step  speculative verify of n_in in-flight tokens per slot
+ *                    from a checkpoint plus a log of per-token inputs; the
+ *                    full state is written only when the log fills.
+ * ssm_copy_step is the copy-state-per-draft verify used as the measurement
+ * baseline of the replay path.
+ *
+ * Conventions (all entry points):
+ *  - Ownership.  The caller allocates and frees every device buffer (state,
+ *    inputs, outputs, replay log, copy buffer, workspace, checkpoints).  The
+ *    library never frees them.  It owns its host metadata and, per handle, one
+ *    small device buffer (checksum and finite-check flags, 4 KiB) allocated on
+ *    first use and freed by ssm_destroy.
+ *  - Pointers named d_* or documented "device" are device pointers; h_* are
+ *    host pointers read before the call returns.  x, dt, B, C, y use the
+ *    handle's io dtype; state, checkpoints, A and D are fp32.
+ *  - Layouts are row-major, last index fastest:
+ *      state[S,H,P,N]  x,y[L,H,P]  dt[L,H]  B,C[L,G,N]  A,D[H]
+ *    (for batched calls the leading L is the batch, or batch*n_in).
+ *  - Ordering.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Results are valid after the stream has synchronised.  Calls on
+ *    one handle must not run concurrently from several host threads.
+ *  - Errors.  Every error detectable on the host is returned before anything
+ *    is enqueued, with state and metadata unchanged.  ssm_last_error() gives
+ *    a message for the calling thread.
+ *  - Metadata is exact.  Positions (tokens since the stream's start or last
+ *    reset) and chunk sequence numbers are host integers the kernels never
+ *    write.
+ */
+#ifndef SSM_STREAM_H
+#define SSM_STREAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_E_INVALID_ARG = -1,   /* bad size, pointer, slot id, dtype ... */
+  SSM_E_INVALID_CHUNK = -2, /* non-finite input (with SSM_FLAG_CHECK_FINITE) */
+  SSM_E_INVALID_STATE = -3, /* unknown or destroyed handle */
+  SSM_E_SEQUENCE = -4,      /* chunk_seq reordered or duplicated */
+  SSM_E_SCHEMA = -5,        /* restore receipt incompatible with the handle */
+  SSM_E_LOG = -6,           /* replay/copy bookkeeping misuse */
+  SSM_E_HIP = -7            /* the HIP runtime reported an error */
+} ssm_status;
+
+/* dtype codes, the same numbering as the pion state_blob format ("SSM.PREFIX.*
+ * -- recurrent-state companion", state_blob section): 0 fp32, 1 fp16, 2 bf16. */
+typedef enum { SSM_F32 = 0, SSM_F16 = 1, SSM_BF16 = 2 } ssm_dtype;
+
+/* Handle creation flags. */
+#define SSM_FLAG_CHECK_FINITE 1u /* scan/decode/replay/copy first check their
+                                    inputs on the device and synchronise; a
+                                    non-finite value returns SSM_E_INVALID_CHUNK
+                                    with nothing changed (the runnable
+                                    artifact's "invalid_chunk") */
+
+/* Layer description.  Supported: H,P >= 1; N % 4 == 0 and 4 <= N <= 128;
+ * G >= 1 with H % G == 0; io_dtype SSM_F32 or SSM_BF16. */
+typedef struct {
+  int32_t H, P, N, G;
+  int32_t io_dtype;        /* ssm_dtype of x, dt, B, C and y */
+  uint32_t schema_version; /* caller's state-schema version */
+  uint64_t model_rev;      /* caller's model revision */
+} ssm_layer_desc;
+
+/* Checkpoint receipt: the fields a resume must match ("Mamba Streaming State
+ * That Survives Chunking", section "Make reset, checkpoint, and cancellation
+ * observable": stream id, model and code revision, schema version, dtype,
+ * dimensions, absolute position, chunk sequence and checksum). */
+typedef struct {
+  uint64_t stream_id;      /* opaque id the library gave the slot's stream */
+  uint64_t model_rev;
+  uint64_t code_rev;       /* ssm_code_rev() of the library that wrote it */
+  uint32_t schema_version;
+  uint32_t state_dtype;    /* always SSM_F32 */
+  int32_t H, P, N, G;
+  int64_t position;        /* tokens since the stream's start or last reset */
+  uint64_t chunk_seq;      /* next chunk sequence number the stream expects */
+  uint64_t checksum;       /* sum over the state's 32-bit words w_i of
+                              w_i * (2*i + 1), modulo 2^64, i in [H,P,N] order */
+} ssm_receipt;
+
+/* Lifecycle counters ("Make reset, checkpoint, and cancellation observable":
+ * keep metrics for resets, duplicate chunks, checkpoints, stale resumes).
+ * Byte counters follow the algorithmic model (state bytes each path must
+ * move), not hardware counters. */
+typedef struct {
+  uint64_t chunks_admitted, chunks_rejected, tokens_scanned, decode_tokens;
+  uint64_t resets, replay_steps, replay_flushes, replay_tokens_committed;
+  uint64_t copy_steps, checkpoints, restores, restores_rejected;
+  uint64_t state_bytes_read, state_bytes_written;
+} ssm_counters;
+
+/* Handles are positive integers; a destroyed handle's id is never reused, so
+ * a call on it returns SSM_E_INVALID_STATE (cancellation is observable). */
+typedef int64_t ssm_handle;
+
+/* ---------------------------------------------------------------- lifecycle */
+
+/* Create a handle over n_slots stream slots whose fp32 state lives in the
+ * caller's d_state[n_slots,H,P,N]; d_A[H], d_D[H] are the layer's fp32
+ * parameters (device, kept by pointer: they must outlive the handle).  Every
+ * slot starts as a fresh stream at position 0 with chunk_seq 0; the caller
+ * decides what d_state holds (ssm_state_reset / ssm_state_init write it).
+ * flags: SSM_FLAG_*.  No device call is made. */
+ssm_status ssm_create(const ssm_layer_desc *desc, int32_t n_slots, float *d_state,
+                      const float *d_A, const float *d_D, uint32_t flags, ssm_handle *out);
+
+/* Cancel: release the handle.  Work already enqueued still completes; any later
+ * call with this handle returns SSM_E_INVALID_STATE. */
+ssm_status ssm_destroy(ssm_handle h);
+
+/* Reset h_slots[n] (distinct): state zeroed on `stream`, position 0, chunk_seq
+ * 0, a new stream id, replay log emptied, any live copy dropped ("Reset
+ * destroys the relationship with the prior stream": section "Make reset,
+ * checkpoint, and cancellation observable"). */
+ssm_status ssm_state_reset(ssm_handle h, int32_t n, const int32_t *h_slots, void *stream);
+
+/* Initialise h_slots[n] from a learned initial state d_init[n,H,P,N] (fp32,
+ * device): as ssm_state_reset but the state is copied from d_init. */
+ssm_status ssm_state_init(ssm_handle h, int32_t n, const int32_t *h_slots, const float *d_init,
+                          void *stream);
+
+/* ----------------------------------------------------------- chunked scan */
+
+/* Bytes of device workspace ssm_scan_chunk may need (H*P*N*4).  It is used
+ * only when a chunk both carries state in (no reset on its first token) and
+ * holds a reset later; otherwise d_workspace may be NULL. */
+size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc);
+
+/* Advance stream `slot` by the L tokens of one chunk.
+ *   chunk_seq   must equal the slot's next expected sequence number (0 after
+ *               create/reset/init); a lower value is a duplicate, a higher one
+ *               a reorder or gap: both return SSM_E_SEQUENCE with nothing
+ *               changed ("Let the full scan define legal chunking": reordering
+ *               or applying a chunk twice must fail).  On success the expected
+ *               number becomes chunk_seq + 1; a retry of a chunk whose result
+ *               was lost must restore a pre-chunk checkpoint first.
+ *   L >= 0      L == 0 (an empty chunk) only advances chunk_seq.
+ *   x[L,H,P] dt[L,H] B,C[L,G,N]  device, io dtype;  y[L,H,P] device, io dtype
+ *   h_reset     host u8[L] or NULL: a nonzero entry zeroes the state and the
+ *               position before that token (a new sequence boundary)
+ *   n_ckpt, h_ckpt_at[n_ckpt]  host, strictly increasing token indices in
+ *               [0,L); the state right after token h_ckpt_at[i] is written to
+ *               d_ckpt_out[i,H,P,N] (device fp32), e.g. each packed
+ *               sequence's final state
+ *   d_workspace, ws_bytes  see ssm_scan_workspace_bytes
+ * The slot's state is the carry-in and receives the carry-out.  The slot must
+ * have no pending replay log or live copy (SSM_E_LOG; see
+ * ssm_state_materialize). */
+ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_t L,
+                          const void *x, const void *dt, const void *B, const void *C,
+                          const uint8_t *h_reset, void *y, int32_t n_ckpt,
+                          const int64_t *h_ckpt_at, float *d_ckpt_out, void *d_workspace,
+                          size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ decode */
+
+/* One token for each of `batch` distinct slots h_slot_ids[batch] ("advances one
+ * or a few positions across many streams": section "Separate Mamba-2 algebra
+ * from kernel behavior").  x[batch,H,P] dt[batch,H] B,C[batch,G,N] in, y[batch,H,P]
+ * out (device, io dtype).  h_reset: host u8[batch] or NULL; a set flag starts
+ * the slot from a zero state (its old state is not read) and position 0, so a
+ * reused batch slot cannot seed its next occupant.  The state is updated in
+ * place.  Slots must have no pending replay log or live copy (SSM_E_LOG). */
+ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                           const void *x, const void *dt, const void *B, const void *C,
+                           const uint8_t *h_reset, void *y, void *stream);
+
+/* ------------------------------------------------------------------ replay */
+
+/* Bytes of the replay log for n_slots slots and window W: per slot W entries of
+ * dt[H], x[H,P] and B[G,N] in the io dtype. */
+size_t ssm_replay_log_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t W);
+
+/* Attach the caller's log buffer (device, ssm_replay_log_bytes bytes) with
+ * window W (1 <= W <= 255).  Every slot's log starts empty; the slot's state
+ * buffer is its checkpoint ("checkpoint: a full copy of the state, written
+ * once per window", Glossary of the speculative-decoding page). */
+ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_bytes);
+
+/* Verify n_in (1 <= n_in <= W) in-flight tokens per slot (the real token plus
+ * drafts).  For each slot, if the committed log length plus n_in exceeds W, the
+ * log is first folded into the checkpoint (the only state write, fused into
+ * this call).  Outputs of every in-flight token are computed from the
+ * checkpoint and the log without writing the state ("The Fix: Log the Inputs,
+ * Checkpoint the State"), and the in-flight inputs are appended to the log.
+ *   x[batch,n_in,H,P] dt[batch,n_in,H] B,C[batch,n_in,G,N]; y[batch,n_in,H,P]
+ * Each slot must then be committed before its next replay step. */
+ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                           const void *x, const void *dt, const void *B, const void *C, void *y,
+                           void *stream);
+
+/* Commit the last replay step of each slot: h_accepted[i] (1..n_in) leading
+ * in-flight tokens join the log and the position; the rest are dropped (they
+ * never enter the committed log).  Host only. */
+ssm_status ssm_replay_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                             const int32_t *h_accepted);
+
+/* -------------------------------------------------- copy-per-draft baseline */
+
+/* Bytes of the copy buffer: n_slots * n_in_max full fp32 states. */
+size_t ssm_copy_buffer_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t n_in_max);
+
+/* Attach the caller's copy buffer d_copies[n_slots,n_in_max,H,P,N] (device). */
+ssm_status ssm_copy_attach(ssm_handle h, int32_t n_in_max, float *d_copies, size_t bytes);
+
+/* Baseline verify ("The Problem": save a full copy of the state after every
+ * draft token): read each slot's live state once, and for each of the n_in
+ * tokens update it, write a full copy and emit the output.  Same layouts as
+ * ssm_replay_step. */
+ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                         const void *x, const void *dt, const void *B, const void *C, void *y,
+                         void *stream);
+
+/* Adopt copy h_accepted[i]-1 as the slot's live state (an index move, no data
+ * copied) and advance the position.  Host only. */
+ssm_status ssm_copy_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                           const int32_t *h_accepted);
+
+/* ------------------------------------------------------ state ops, receipts */
+
+/* Make the slot's state buffer hold its current state: fold a non-empty replay
+ * log into it, or copy a live copy back.  SSM_E_LOG if a replay or copy step
+ * is awaiting commit. */
+ssm_status ssm_state_materialize(ssm_handle h, int32_t n, const int32_t *h_slots, void *stream);
+
+/* Checkpoint `slot`: materialize it, copy its state to d_dst[H,P,N] (device
+ * fp32) and fill *out.  Synchronises `stream` (the checksum is computed on the
+ * device and read back). */
+ssm_status ssm_state_checkpoint(ssm_handle h, int32_t slot, float *d_dst, ssm_receipt *out,
+                                void *stream);
+
+/* Resume `slot` from d_src[H,P,N] and its receipt.  Any semantic mismatch
+ * (schema version, dtype, H, P, N, G, model or code revision) or a checksum
+ * that does not match d_src returns SSM_E_SCHEMA with nothing changed (reject,
+ * never pad or truncate).  Synchronises `stream`. */
+ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
+                             const ssm_receipt *r, void *stream);
+
+/* Read a slot's position and next expected chunk sequence number. */
+ssm_status ssm_get_position(ssm_handle h, int32_t slot, int64_t *pos, uint64_t *chunk_seq);
+
+/* Read the replay log length of a slot (committed entries) and whether a
+ * replay/copy step awaits commit. */
+ssm_status ssm_get_log_state(ssm_handle h, int32_t slot, int32_t *log_len, int32_t *pending);
+
+/* Lifecycle counters of the handle. */
+ssm_status ssm_get_counters(ssm_handle h, ssm_counters *out);
+
+/* --------------------------------------------------------------------- misc */
+
+const char *ssm_last_error(void); /* message of the calling thread's last error */
+uint64_t ssm_code_rev(void);      /* revision of the state semantics and kernels */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_STREAM_H */

@@ -1,0 +1,119 @@
+// ssm_device.h -- device helpers shared by the library's kernels: io-dtype
+// loads/stores (fp32 or bf16 bits), the 64-row state-tile thread layout and
+// the cross-lane row reduction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+
+// ------------------------------------------------------------------ io types
+// fp32 is stored as float, bf16 as its 16-bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f(bf16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Io;
+template <> struct Io<float> {
+  static __device__ __forceinline__ float ld(const float *p) { return *p; }
+  static __device__ __forceinline__ float4 ld4(const float *p) {
+    return *reinterpret_cast<const float4 *>(p);
+  }
+  static __device__ __forceinline__ void st(float *p, float v) { *p = v; }
+  static __device__ __forceinline__ void st4(float *p, float4 v) {
+    *reinterpret_cast<float4 *>(p) = v;
+  }
+};
+template <> struct Io<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t *p) { return bf16_to_f(*p); }
+  static __device__ __forceinline__ float4 ld4(const bf16_t *p) {
+    uint2 r = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  }
+  static __device__ __forceinline__ void st(bf16_t *p, float v) { *p = f_to_bf16(v); }
+  static __device__ __forceinline__ void st4(bf16_t *p, float4 v) {
+    uint2 r;
+    r.x = (uint32_t)f_to_bf16(v.x) | ((uint32_t)f_to_bf16(v.y) << 16);
+    r.y = (uint32_t)f_to_bf16(v.z) | ((uint32_t)f_to_bf16(v.w) << 16);
+    *reinterpret_cast<uint2 *>(p) = r;
+  }
+};
+
+// -------------------------------------------------------- state-tile layout
+// A workgroup of 256 threads (4 waves) owns a 64-row x N tile of one head's
+// fp32 state.  Lane l of wave w holds float4 column c = l & 31 (state entries
+// n = 4c..4c+3) of rows r_i = 8*i + 2*w + (l >> 5), i = 0..7.  One wave-wide
+// load instruction therefore covers two adjacent rows (2 * 512 B contiguous
+// at N = 128).
+struct Tile {
+  int lane, wave, c, rsub;
+  __device__ __forceinline__ Tile() {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    c = lane & 31;
+    rsub = lane >> 5;
+  }
+  __device__ __forceinline__ int row(int i) const { return 8 * i + 2 * wave + rsub; }
+  // Row (within the tile) whose total this lane holds after reduce8().
+  __device__ __forceinline__ int reduced_row() const {
+    int r = ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+    return row(r);
+  }
+  // One lane of each group of four that hold the same reduced total.
+  __device__ __forceinline__ bool reduced_writer() const { return (lane & 3) == 0; }
+};
+
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+__device__ __forceinline__ float4 fma4(float s, float4 h, float u, float4 b) {
+  return make_float4(s * h.x + u * b.x, s * h.y + u * b.y, s * h.z + u * b.z, s * h.w + u * b.w);
+}
+
+// Sum eight per-row partials across the 32 lanes of a row group by recursive
+// halving: each exchange step halves the number of values a lane carries.
+// Returns the total of row reduced_row() of the calling lane.
+__device__ __forceinline__ float halve(float lo, float hi, int bit, int mask) {
+  float send = bit ? lo : hi;
+  float recv = __shfl_xor(send, mask);
+  return (bit ? hi : lo) + recv;
+}
+__device__ __forceinline__ float reduce8(const float v[8], int lane) {
+  const int b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+  float s4[4], s2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4[i] = halve(v[i], v[i + 4], b4, 16);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) s2[i] = halve(s4[i], s4[i + 2], b3, 8);
+  float s = halve(s2[0], s2[1], b2, 4);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  return s;
+}
+
+// Streaming (nontemporal) 128-bit state accesses: the state is touched once
+// per step and the working set is far larger than the caches.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 nt_load4(const float *p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store4(float *p, float4 v) {
+  const f32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t *>(p));
+}
+
+}  // namespace ssm

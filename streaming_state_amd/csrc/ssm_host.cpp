@@ -1,0 +1,879 @@
+// ssm_host.cpp -- host runtime behind include/ssm_stream.h: handles, argument
+// and lifecycle validation, exact integer metadata (positions, chunk sequence
+// numbers, replay log lengths, live copies), and kernel launches on the
+// caller's stream.  Every check runs before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <initializer_list>
+#include <utility>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/ssm_stream.h"
+#include "ssm_internal.h"
+
+using namespace ssm;
+
+namespace {
+
+constexpr uint64_t kCodeRev = 1;
+
+thread_local std::string t_err;
+
+ssm_status fail(ssm_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_err = buf;
+  return st;
+}
+
+enum Pend { kNone = 0, kReplayPend = 1, kCopyPend = 2 };
+
+struct Slot {
+  int64_t pos = 0;
+  uint64_t chunk_seq = 0;
+  uint64_t stream_id = 0;
+  int log_len = 0;    // committed replay log entries
+  int log_half = 0;   // half of the log that holds them
+  int pend = kNone;   // a verify step awaits commit
+  int pend_n = 0;     // its n_in
+  int pend_base = 0;  // replay: committed length the step saw
+  int live = -1;      // copy baseline: live copy index, -1 = the state buffer
+};
+
+struct Handle {
+  ssm_layer_desc desc;
+  Dims d;
+  int io;
+  int S;
+  float *state;
+  const float *A, *D;
+  uint32_t flags;
+  std::vector<Slot> slots;
+  std::vector<uint32_t> stamp;  // per-slot epoch marks for distinctness checks
+  uint32_t epoch = 0;
+  // replay
+  int W = 0;
+  void *log = nullptr;
+  LogLayout lay{};
+  // copy baseline
+  int n_in_max = 0;
+  float *copies = nullptr;
+  // device scratch: [0] checksum accumulator (u64), [1] finite flag (u32)
+  void *scratch = nullptr;
+  ssm_counters cnt{};
+  size_t state_bytes() const { return (size_t)d.H * d.P * d.N * sizeof(float); }
+  float *slot_state(int s) const { return state + (size_t)s * d.H * d.P * d.N; }
+};
+
+std::mutex g_mu;
+std::unordered_map<int64_t, Handle *> g_handles;
+int64_t g_next_handle = 1;
+uint64_t g_next_stream = 1;
+
+Handle *lookup(ssm_handle h) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_handles.find(h);
+  return it == g_handles.end() ? nullptr : it->second;
+}
+
+uint64_t new_stream_id() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_next_stream++;
+}
+
+#define GET_HANDLE(var, h)                                                              \
+  Handle *var = lookup(h);                                                              \
+  if (!var) return fail(SSM_E_INVALID_STATE, "handle %lld is not live", (long long)(h))
+
+#define HIP_TRY(expr)                                                          \
+  do {                                                                         \
+    hipError_t e_ = (expr);                                                    \
+    if (e_ != hipSuccess)                                                      \
+      return fail(SSM_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));   \
+  } while (0)
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+size_t io_size(int io) { return io == kBF16 ? 2 : 4; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The kernels load B and C rows four elements at a time and the state as
+// float4: x, dt, y must be aligned to the element size, B and C to four
+// elements, fp32 state buffers to 16 bytes.
+ssm_status check_io_align(int io, const void *x, const void *dt, const void *B, const void *C,
+                          const void *y, const char *what) {
+  const size_t es = io_size(io);
+  if (!aligned(x, es) || !aligned(dt, es) || !aligned(y, es) || !aligned(B, 4 * es) ||
+      !aligned(C, 4 * es))
+    return fail(SSM_E_INVALID_ARG, "%s: misaligned input or output pointer", what);
+  return SSM_OK;
+}
+
+ssm_status check_desc(const ssm_layer_desc *desc) {
+  if (!desc) return fail(SSM_E_INVALID_ARG, "desc is NULL");
+  if (desc->H < 1 || desc->P < 1 || desc->G < 1 || desc->H % desc->G != 0)
+    return fail(SSM_E_INVALID_ARG, "need H, P, G >= 1 and H %% G == 0 (H=%d P=%d G=%d)",
+                desc->H, desc->P, desc->G);
+  if (desc->N < 4 || desc->N > kMaxN || desc->N % 4 != 0)
+    return fail(SSM_E_INVALID_ARG, "N must be a multiple of 4 in [4, %d] (N=%d)", kMaxN,
+                desc->N);
+  if (desc->io_dtype != SSM_F32 && desc->io_dtype != SSM_BF16)
+    return fail(SSM_E_INVALID_ARG, "io_dtype %d not supported (fp32 or bf16)", desc->io_dtype);
+  return SSM_OK;
+}
+
+// Validate a batch of slot ids: in range and pairwise distinct.
+ssm_status check_slots(Handle *H, int n, const int32_t *slots, const char *what) {
+  if (n < 0) return fail(SSM_E_INVALID_ARG, "%s: negative count", what);
+  if (n > 0 && !slots) return fail(SSM_E_INVALID_ARG, "%s: slot ids are NULL", what);
+  if (++H->epoch == 0) {
+    std::fill(H->stamp.begin(), H->stamp.end(), 0u);
+    H->epoch = 1;
+  }
+  for (int i = 0; i < n; ++i) {
+    const int s = slots[i];
+    if (s < 0 || s >= H->S) return fail(SSM_E_INVALID_ARG, "%s: slot %d out of range", what, s);
+    if (H->stamp[s] == H->epoch) return fail(SSM_E_INVALID_ARG, "%s: slot %d repeated", what, s);
+    H->stamp[s] = H->epoch;
+  }
+  return SSM_OK;
+}
+
+ssm_status ensure_scratch(Handle *H) {
+  if (H->scratch) return SSM_OK;
+  HIP_TRY(hipMalloc(&H->scratch, 4096));
+  return SSM_OK;
+}
+
+// Device-side finite check of a list of io-dtype buffers; synchronises.
+ssm_status check_finite(Handle *H, hipStream_t s, std::initializer_list<std::pair<const void *, size_t>> bufs) {
+  if (!(H->flags & SSM_FLAG_CHECK_FINITE)) return SSM_OK;
+  ssm_status st = ensure_scratch(H);
+  if (st != SSM_OK) return st;
+  unsigned int *flag = reinterpret_cast<unsigned int *>((char *)H->scratch + 64);
+  HIP_TRY(launch_zero_u64(reinterpret_cast<unsigned long long *>(flag), 1, s));
+  for (auto &b : bufs) HIP_TRY(launch_finite_check(H->io, b.first, b.second, flag, s));
+  unsigned int host = 0;
+  HIP_TRY(hipMemcpyAsync(&host, flag, sizeof host, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (host) return fail(SSM_E_INVALID_CHUNK, "non-finite input");
+  return SSM_OK;
+}
+
+ssm_status device_checksum(Handle *H, const float *src, hipStream_t s, uint64_t *out) {
+  ssm_status st = ensure_scratch(H);
+  if (st != SSM_OK) return st;
+  unsigned long long *acc = reinterpret_cast<unsigned long long *>(H->scratch);
+  HIP_TRY(launch_zero_u64(acc, 1, s));
+  HIP_TRY(launch_checksum(src, H->state_bytes() / 4, acc, s));
+  unsigned long long host = 0;
+  HIP_TRY(hipMemcpyAsync(&host, acc, sizeof host, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  *out = host;
+  return SSM_OK;
+}
+
+ssm_status slot_is_plain(Handle *H, int s, const char *what) {
+  const Slot &sl = H->slots[s];
+  if (sl.pend != kNone)
+    return fail(SSM_E_LOG, "%s: slot %d has a verify step awaiting commit", what, s);
+  if (sl.log_len > 0 || sl.live >= 0)
+    return fail(SSM_E_LOG, "%s: slot %d holds a replay log or live copy (materialize it first)",
+                what, s);
+  return SSM_OK;
+}
+
+void fresh_stream(Slot &sl) {
+  sl.pos = 0;
+  sl.chunk_seq = 0;
+  sl.stream_id = new_stream_id();
+  sl.log_len = 0;
+  sl.pend = kNone;
+  sl.pend_n = 0;
+  sl.live = -1;
+}
+
+// Fold the replay log of the given slots into their checkpoints (n_in = 0).
+ssm_status fold_logs(Handle *H, const std::vector<int> &slots, hipStream_t s) {
+  for (size_t i0 = 0; i0 < slots.size(); i0 += kBatchPerLaunch) {
+    const int n = (int)std::min<size_t>(kBatchPerLaunch, slots.size() - i0);
+    ReplayMeta m;
+    for (int i = 0; i < n; ++i) {
+      Slot &sl = H->slots[slots[i0 + i]];
+      m.slot[i] = slots[i0 + i];
+      m.fold_len[i] = (uint8_t)sl.log_len;
+      m.base_len[i] = 0;
+      m.halves[i] = (uint8_t)(sl.log_half | ((1 - sl.log_half) << 1));
+    }
+    ReplayArgs a{};
+    a.state = H->state;
+    a.log = H->log;
+    a.bc = reinterpret_cast<float *>((char *)H->log + H->lay.bc_off);
+    a.A = H->A;
+    a.D = H->D;
+    a.d = H->d;
+    a.n = n;
+    a.n_in = 0;
+    a.W = H->W;
+    HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
+  }
+  for (int sidx : slots) {
+    Slot &sl = H->slots[sidx];
+    sl.log_half = 1 - sl.log_half;
+    sl.log_len = 0;
+    H->cnt.replay_flushes++;
+    H->cnt.state_bytes_read += H->state_bytes();
+    H->cnt.state_bytes_written += H->state_bytes();
+  }
+  return SSM_OK;
+}
+
+ssm_status materialize(Handle *H, int n, const int32_t *slots, hipStream_t s) {
+  std::vector<int> folds;
+  for (int i = 0; i < n; ++i) {
+    const Slot &sl = H->slots[slots[i]];
+    if (sl.pend != kNone)
+      return fail(SSM_E_LOG, "materialize: slot %d has a verify step awaiting commit", slots[i]);
+  }
+  for (int i = 0; i < n; ++i) {
+    Slot &sl = H->slots[slots[i]];
+    if (sl.log_len > 0) folds.push_back(slots[i]);
+  }
+  if (!folds.empty()) {
+    ssm_status st = fold_logs(H, folds, s);
+    if (st != SSM_OK) return st;
+  }
+  const size_t nf = H->state_bytes() / 4;
+  for (int i = 0; i < n; ++i) {
+    Slot &sl = H->slots[slots[i]];
+    if (sl.live >= 0) {
+      const float *src = H->copies + ((size_t)slots[i] * H->n_in_max + sl.live) * nf;
+      HIP_TRY(launch_copy_f32(H->slot_state(slots[i]), src, nf, s));
+      sl.live = -1;
+    }
+  }
+  return SSM_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char *ssm_last_error(void) { return t_err.c_str(); }
+uint64_t ssm_code_rev(void) { return kCodeRev; }
+
+ssm_status ssm_create(const ssm_layer_desc *desc, int32_t n_slots, float *d_state,
+                      const float *d_A, const float *d_D, uint32_t flags, ssm_handle *out) {
+  ssm_status st = check_desc(desc);
+  if (st != SSM_OK) return st;
+  if (!out) return fail(SSM_E_INVALID_ARG, "out is NULL");
+  if (n_slots < 1) return fail(SSM_E_INVALID_ARG, "n_slots must be >= 1");
+  if (!d_state || !d_A || !d_D) return fail(SSM_E_INVALID_ARG, "state, A and D are required");
+  if (flags & ~SSM_FLAG_CHECK_FINITE) return fail(SSM_E_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!aligned(d_state, 16)) return fail(SSM_E_INVALID_ARG, "state must be 16-byte aligned");
+  Handle *H = new Handle();
+  H->desc = *desc;
+  H->d = Dims{desc->H, desc->P, desc->N, desc->G, (desc->P + kRows - 1) / kRows};
+  H->io = desc->io_dtype;
+  H->S = n_slots;
+  H->state = d_state;
+  H->A = d_A;
+  H->D = d_D;
+  H->flags = flags;
+  H->slots.resize(n_slots);
+  H->stamp.assign(n_slots, 0u);
+  for (auto &sl : H->slots) fresh_stream(sl);
+  std::lock_guard<std::mutex> lk(g_mu);
+  const int64_t id = g_next_handle++;
+  g_handles[id] = H;
+  *out = id;
+  return SSM_OK;
+}
+
+ssm_status ssm_destroy(ssm_handle h) {
+  Handle *H = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_handles.find(h);
+    if (it == g_handles.end())
+      return fail(SSM_E_INVALID_STATE, "handle %lld is not live", (long long)h);
+    H = it->second;
+    g_handles.erase(it);
+  }
+  if (H->scratch) {
+    // work already enqueued may still use the scratch buffer
+    (void)hipDeviceSynchronize();
+    (void)hipFree(H->scratch);
+  }
+  delete H;
+  return SSM_OK;
+}
+
+static ssm_status reset_or_init(ssm_handle h, int32_t n, const int32_t *slots, const float *init,
+                                void *stream, const char *what) {
+  GET_HANDLE(H, h);
+  ssm_status st = check_slots(H, n, slots, what);
+  if (st != SSM_OK) return st;
+  for (int i = 0; i < n; ++i)
+    if (H->slots[slots[i]].pend != kNone)
+      return fail(SSM_E_LOG, "%s: slot %d has a verify step awaiting commit", what, slots[i]);
+  hipStream_t s = as_stream(stream);
+  const size_t nf = H->state_bytes() / 4;
+  for (int i = 0; i < n; ++i) {
+    if (init)
+      HIP_TRY(launch_copy_f32(H->slot_state(slots[i]), init + (size_t)i * nf, nf, s));
+    else
+      HIP_TRY(launch_zero(H->slot_state(slots[i]), nf, s));
+  }
+  for (int i = 0; i < n; ++i) fresh_stream(H->slots[slots[i]]);
+  H->cnt.resets += n;
+  H->cnt.state_bytes_written += (size_t)n * H->state_bytes();
+  return SSM_OK;
+}
+
+ssm_status ssm_state_reset(ssm_handle h, int32_t n, const int32_t *h_slots, void *stream) {
+  return reset_or_init(h, n, h_slots, nullptr, stream, "ssm_state_reset");
+}
+
+ssm_status ssm_state_init(ssm_handle h, int32_t n, const int32_t *h_slots, const float *d_init,
+                          void *stream) {
+  if (!d_init || !aligned(d_init, 16))
+    return fail(SSM_E_INVALID_ARG, "ssm_state_init: d_init must be non-NULL and 16-byte aligned");
+  return reset_or_init(h, n, h_slots, d_init, stream, "ssm_state_init");
+}
+
+// ------------------------------------------------------------------- scan
+size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc) {
+  if (!desc || desc->H < 1 || desc->P < 1 || desc->N < 1) return 0;
+  return (size_t)desc->H * desc->P * desc->N * sizeof(float);
+}
+
+ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_t L,
+                          const void *x, const void *dt, const void *B, const void *C,
+                          const uint8_t *h_reset, void *y, int32_t n_ckpt,
+                          const int64_t *h_ckpt_at, float *d_ckpt_out, void *d_workspace,
+                          size_t ws_bytes, void *stream) {
+  GET_HANDLE(H, h);
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "scan: slot %d out of range", slot);
+  Slot &sl = H->slots[slot];
+  if (chunk_seq != sl.chunk_seq) {
+    H->cnt.chunks_rejected++;
+    return fail(SSM_E_SEQUENCE, "scan: slot %d expects chunk %llu, got %llu (%s)", slot,
+                (unsigned long long)sl.chunk_seq, (unsigned long long)chunk_seq,
+                chunk_seq < sl.chunk_seq ? "duplicate" : "reordered or gap");
+  }
+  ssm_status st = slot_is_plain(H, slot, "scan");
+  if (st != SSM_OK) return st;
+  if (L < 0 || L > (int64_t)INT32_MAX) return fail(SSM_E_INVALID_ARG, "scan: bad L %lld", (long long)L);
+  if (n_ckpt < 0 || n_ckpt > kCkptPerLaunch)
+    return fail(SSM_E_INVALID_ARG, "scan: n_ckpt must be in [0, %d]", kCkptPerLaunch);
+  if (n_ckpt > 0 && (!h_ckpt_at || !d_ckpt_out))
+    return fail(SSM_E_INVALID_ARG, "scan: checkpoints need h_ckpt_at and d_ckpt_out");
+  for (int i = 0; i < n_ckpt; ++i) {
+    if (h_ckpt_at[i] < 0 || h_ckpt_at[i] >= L)
+      return fail(SSM_E_INVALID_ARG, "scan: checkpoint %d at token %lld outside [0, L)", i,
+                  (long long)h_ckpt_at[i]);
+    if (i > 0 && h_ckpt_at[i] <= h_ckpt_at[i - 1])
+      return fail(SSM_E_INVALID_ARG, "scan: checkpoint tokens must increase");
+  }
+  if (L == 0) {  // an empty chunk is legal: it only advances the sequence number
+    sl.chunk_seq++;
+    H->cnt.chunks_admitted++;
+    return SSM_OK;
+  }
+  if (!x || !dt || !B || !C || !y) return fail(SSM_E_INVALID_ARG, "scan: NULL input or output");
+  st = check_io_align(H->io, x, dt, B, C, y, "scan");
+  if (st != SSM_OK) return st;
+  if ((n_ckpt > 0 && !aligned(d_ckpt_out, 16)) || !aligned(d_workspace, 16))
+    return fail(SSM_E_INVALID_ARG, "scan: checkpoint and workspace buffers must be 16-byte aligned");
+  // segments: runs between resets
+  std::vector<ScanSeg> segs;
+  {
+    int32_t t0 = 0;
+    const bool first_init = !(h_reset && h_reset[0]);
+    for (int64_t t = 1; t <= L; ++t) {
+      if (t == L || (h_reset && h_reset[t])) {
+        segs.push_back(ScanSeg{t0, (int32_t)t, (int32_t)(segs.empty() ? first_init : 0), 0});
+        t0 = (int32_t)t;
+      }
+    }
+  }
+  const bool need_ws = segs.size() > 1 && segs.front().init;
+  segs.back().final = need_ws ? 2 : 1;
+  if (need_ws && (!d_workspace || ws_bytes < H->state_bytes()))
+    return fail(SSM_E_INVALID_ARG,
+                "scan: this chunk carries state in and resets later; it needs a workspace of "
+                "%zu bytes",
+                H->state_bytes());
+  hipStream_t s = as_stream(stream);
+  const size_t es = io_size(H->io);
+  st = check_finite(H, s, {{x, (size_t)L * H->d.H * H->d.P}, {dt, (size_t)L * H->d.H},
+                           {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
+  if (st != SSM_OK) return st;
+  (void)es;
+  for (size_t i0 = 0; i0 < segs.size(); i0 += kSegPerLaunch) {
+    const int ns = (int)std::min<size_t>(kSegPerLaunch, segs.size() - i0);
+    ScanMeta m{};
+    for (int i = 0; i < ns; ++i) m.seg[i] = segs[i0 + i];
+    const int32_t lo = segs[i0].t0, hi = segs[i0 + ns - 1].t1;
+    int nck = 0;
+    for (int i = 0; i < n_ckpt; ++i)
+      if (h_ckpt_at[i] >= lo && h_ckpt_at[i] < hi) {
+        m.ck_t[nck] = (int32_t)h_ckpt_at[i];
+        m.ck_idx[nck] = i;
+        ++nck;
+      }
+    ScanArgs a{};
+    a.x = x;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.y = y;
+    a.state = H->slot_state(slot);
+    a.workspace = (float *)d_workspace;
+    a.ckpt_out = d_ckpt_out;
+    a.A = H->A;
+    a.D = H->D;
+    a.d = H->d;
+    a.n_seg = ns;
+    a.n_ck = nck;
+    HIP_TRY(launch_scan(H->io, a, m, s));
+  }
+  if (need_ws)
+    HIP_TRY(launch_copy_f32(H->slot_state(slot), (const float *)d_workspace,
+                            H->state_bytes() / 4, s));
+  // exact host metadata
+  int64_t pos = sl.pos;
+  for (int64_t t = 0; t < L; ++t) {
+    if (h_reset && h_reset[t]) pos = 0;
+    pos += 1;
+  }
+  sl.pos = pos;
+  sl.chunk_seq++;
+  H->cnt.chunks_admitted++;
+  H->cnt.tokens_scanned += (uint64_t)L;
+  if (segs.front().init) H->cnt.state_bytes_read += H->state_bytes();
+  H->cnt.state_bytes_written += H->state_bytes() * (1 + (size_t)n_ckpt);
+  return SSM_OK;
+}
+
+// ----------------------------------------------------------------- decode
+ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                           const void *x, const void *dt, const void *B, const void *C,
+                           const uint8_t *h_reset, void *y, void *stream) {
+  GET_HANDLE(H, h);
+  ssm_status st = check_slots(H, batch, h_slot_ids, "decode");
+  if (st != SSM_OK) return st;
+  for (int i = 0; i < batch; ++i) {
+    st = slot_is_plain(H, h_slot_ids[i], "decode");
+    if (st != SSM_OK) return st;
+  }
+  if (batch == 0) return SSM_OK;
+  if (!x || !dt || !B || !C || !y) return fail(SSM_E_INVALID_ARG, "decode: NULL input or output");
+  st = check_io_align(H->io, x, dt, B, C, y, "decode");
+  if (st != SSM_OK) return st;
+  hipStream_t s = as_stream(stream);
+  const Dims &d = H->d;
+  st = check_finite(H, s, {{x, (size_t)batch * d.H * d.P}, {dt, (size_t)batch * d.H},
+                           {B, (size_t)batch * d.G * d.N}, {C, (size_t)batch * d.G * d.N}});
+  if (st != SSM_OK) return st;
+  const size_t es = io_size(H->io);
+  for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
+    const int n = std::min(kBatchPerLaunch, batch - i0);
+    DecodeMeta m;
+    for (int i = 0; i < n; ++i) {
+      m.slot[i] = h_slot_ids[i0 + i];
+      m.reset[i] = h_reset ? (h_reset[i0 + i] != 0) : 0;
+    }
+    DecodeArgs a{};
+    a.x = (const char *)x + (size_t)i0 * d.H * d.P * es;
+    a.dt = (const char *)dt + (size_t)i0 * d.H * es;
+    a.B = (const char *)B + (size_t)i0 * d.G * d.N * es;
+    a.C = (const char *)C + (size_t)i0 * d.G * d.N * es;
+    a.y = (char *)y + (size_t)i0 * d.H * d.P * es;
+    a.state = H->state;
+    a.A = H->A;
+    a.D = H->D;
+    a.d = d;
+    a.n = n;
+    HIP_TRY(launch_decode(H->io, a, m, s));
+  }
+  for (int i = 0; i < batch; ++i) {
+    Slot &sl = H->slots[h_slot_ids[i]];
+    const bool r = h_reset && h_reset[i];
+    if (r) {
+      sl.pos = 0;
+      H->cnt.resets++;
+    } else {
+      H->cnt.state_bytes_read += H->state_bytes();
+    }
+    sl.pos += 1;
+    H->cnt.state_bytes_written += H->state_bytes();
+  }
+  H->cnt.decode_tokens += batch;
+  return SSM_OK;
+}
+
+// ----------------------------------------------------------------- replay
+size_t ssm_replay_log_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t W) {
+  if (check_desc(desc) != SSM_OK || n_slots < 1 || W < 1 || W > kMaxW) return 0;
+  const Dims d{desc->H, desc->P, desc->N, desc->G, (desc->P + kRows - 1) / kRows};
+  return log_layout(desc->io_dtype, d, n_slots, W).total;
+}
+
+ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_bytes) {
+  GET_HANDLE(H, h);
+  if (W < 1 || W > kMaxW) return fail(SSM_E_INVALID_ARG, "replay: W must be in [1, %d]", kMaxW);
+  if (!d_log || !aligned(d_log, 256))
+    return fail(SSM_E_INVALID_ARG, "replay: log must be non-NULL and 256-byte aligned");
+  const LogLayout lay = log_layout(H->io, H->d, H->S, W);
+  if (log_bytes < lay.total)
+    return fail(SSM_E_INVALID_ARG, "replay: log needs %zu bytes, got %zu", lay.total, log_bytes);
+  for (int s = 0; s < H->S; ++s)
+    if (H->slots[s].log_len > 0 || H->slots[s].pend != kNone)
+      return fail(SSM_E_LOG, "replay: slot %d still uses the current log", s);
+  H->W = W;
+  H->log = d_log;
+  H->lay = lay;
+  for (auto &sl : H->slots) {
+    sl.log_len = 0;
+    sl.log_half = 0;
+  }
+  return SSM_OK;
+}
+
+ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                           const void *x, const void *dt, const void *B, const void *C, void *y,
+                           void *stream) {
+  GET_HANDLE(H, h);
+  if (!H->log) return fail(SSM_E_LOG, "replay: no log attached");
+  if (n_in < 1 || n_in > H->W || n_in > kMaxInFlight)
+    return fail(SSM_E_INVALID_ARG, "replay: n_in must be in [1, min(W, %d)]", kMaxInFlight);
+  ssm_status st = check_slots(H, batch, h_slot_ids, "replay");
+  if (st != SSM_OK) return st;
+  for (int i = 0; i < batch; ++i) {
+    const Slot &sl = H->slots[h_slot_ids[i]];
+    if (sl.pend != kNone)
+      return fail(SSM_E_LOG, "replay: slot %d has a verify step awaiting commit", h_slot_ids[i]);
+    if (sl.live >= 0)
+      return fail(SSM_E_LOG, "replay: slot %d holds a live copy (materialize it first)",
+                  h_slot_ids[i]);
+  }
+  if (batch == 0) return SSM_OK;
+  if (!x || !dt || !B || !C || !y) return fail(SSM_E_INVALID_ARG, "replay: NULL input or output");
+  st = check_io_align(H->io, x, dt, B, C, y, "replay");
+  if (st != SSM_OK) return st;
+  hipStream_t s = as_stream(stream);
+  const Dims &d = H->d;
+  const size_t nt = (size_t)batch * n_in;
+  st = check_finite(H, s, {{x, nt * d.H * d.P}, {dt, nt * d.H}, {B, nt * d.G * d.N},
+                           {C, nt * d.G * d.N}});
+  if (st != SSM_OK) return st;
+  const size_t es = io_size(H->io);
+  for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
+    const int n = std::min(kBatchPerLaunch, batch - i0);
+    ReplayMeta m;
+    for (int i = 0; i < n; ++i) {
+      const Slot &sl = H->slots[h_slot_ids[i0 + i]];
+      m.slot[i] = h_slot_ids[i0 + i];
+      if (sl.log_len + n_in > H->W) {  // the log is full: fold, then start the other half
+        m.fold_len[i] = (uint8_t)sl.log_len;
+        m.base_len[i] = 0;
+        m.halves[i] = (uint8_t)(sl.log_half | ((1 - sl.log_half) << 1));
+      } else {
+        m.fold_len[i] = 0;
+        m.base_len[i] = (uint8_t)sl.log_len;
+        m.halves[i] = (uint8_t)(sl.log_half | (sl.log_half << 1));
+      }
+    }
+    const size_t off = (size_t)i0 * n_in;
+    ReplayArgs a{};
+    a.x = (const char *)x + off * d.H * d.P * es;
+    a.dt = (const char *)dt + off * d.H * es;
+    a.B = (const char *)B + off * d.G * d.N * es;
+    a.C = (const char *)C + off * d.G * d.N * es;
+    a.y = (char *)y + off * d.H * d.P * es;
+    a.state = H->state;
+    a.log = H->log;
+    a.bc = reinterpret_cast<float *>((char *)H->log + H->lay.bc_off);
+    a.A = H->A;
+    a.D = H->D;
+    a.d = d;
+    a.n = n;
+    a.n_in = n_in;
+    a.W = H->W;
+    HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
+  }
+  for (int i = 0; i < batch; ++i) {
+    Slot &sl = H->slots[h_slot_ids[i]];
+    if (sl.log_len + n_in > H->W) {
+      sl.log_half = 1 - sl.log_half;
+      sl.log_len = 0;
+      H->cnt.replay_flushes++;
+      H->cnt.state_bytes_written += H->state_bytes();
+    }
+    sl.pend = kReplayPend;
+    sl.pend_n = n_in;
+    sl.pend_base = sl.log_len;
+    H->cnt.state_bytes_read += H->state_bytes();
+  }
+  H->cnt.replay_steps++;
+  return SSM_OK;
+}
+
+ssm_status ssm_replay_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                             const int32_t *h_accepted) {
+  GET_HANDLE(H, h);
+  ssm_status st = check_slots(H, batch, h_slot_ids, "replay commit");
+  if (st != SSM_OK) return st;
+  if (batch > 0 && !h_accepted) return fail(SSM_E_INVALID_ARG, "replay commit: accepted is NULL");
+  for (int i = 0; i < batch; ++i) {
+    const Slot &sl = H->slots[h_slot_ids[i]];
+    if (sl.pend != kReplayPend)
+      return fail(SSM_E_LOG, "replay commit: slot %d has no replay step to commit", h_slot_ids[i]);
+    if (h_accepted[i] < 1 || h_accepted[i] > sl.pend_n)
+      return fail(SSM_E_LOG, "replay commit: slot %d accepted %d outside [1, %d]", h_slot_ids[i],
+                  h_accepted[i], sl.pend_n);
+  }
+  for (int i = 0; i < batch; ++i) {
+    Slot &sl = H->slots[h_slot_ids[i]];
+    sl.log_len = sl.pend_base + h_accepted[i];
+    sl.pos += h_accepted[i];
+    sl.pend = kNone;
+    sl.pend_n = 0;
+    H->cnt.replay_tokens_committed += h_accepted[i];
+  }
+  return SSM_OK;
+}
+
+// ---------------------------------------------------------- copy baseline
+size_t ssm_copy_buffer_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t n_in_max) {
+  if (check_desc(desc) != SSM_OK || n_slots < 1 || n_in_max < 1) return 0;
+  return (size_t)n_slots * n_in_max * desc->H * desc->P * desc->N * sizeof(float);
+}
+
+ssm_status ssm_copy_attach(ssm_handle h, int32_t n_in_max, float *d_copies, size_t bytes) {
+  GET_HANDLE(H, h);
+  if (n_in_max < 1 || n_in_max > 127)
+    return fail(SSM_E_INVALID_ARG, "copy: n_in_max must be in [1, 127]");
+  if (!d_copies || !aligned(d_copies, 16))
+    return fail(SSM_E_INVALID_ARG, "copy: buffer must be non-NULL and 16-byte aligned");
+  const size_t need = (size_t)H->S * n_in_max * H->state_bytes();
+  if (bytes < need) return fail(SSM_E_INVALID_ARG, "copy: need %zu bytes, got %zu", need, bytes);
+  for (int s = 0; s < H->S; ++s)
+    if (H->slots[s].live >= 0 || H->slots[s].pend == kCopyPend)
+      return fail(SSM_E_LOG, "copy: slot %d still uses the current buffer", s);
+  H->n_in_max = n_in_max;
+  H->copies = d_copies;
+  return SSM_OK;
+}
+
+ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                         const void *x, const void *dt, const void *B, const void *C, void *y,
+                         void *stream) {
+  GET_HANDLE(H, h);
+  if (!H->copies) return fail(SSM_E_LOG, "copy: no buffer attached");
+  if (n_in < 1 || n_in > H->n_in_max)
+    return fail(SSM_E_INVALID_ARG, "copy: n_in must be in [1, %d]", H->n_in_max);
+  ssm_status st = check_slots(H, batch, h_slot_ids, "copy");
+  if (st != SSM_OK) return st;
+  for (int i = 0; i < batch; ++i) {
+    const Slot &sl = H->slots[h_slot_ids[i]];
+    if (sl.pend != kNone)
+      return fail(SSM_E_LOG, "copy: slot %d has a verify step awaiting commit", h_slot_ids[i]);
+    if (sl.log_len > 0)
+      return fail(SSM_E_LOG, "copy: slot %d holds a replay log (materialize it first)",
+                  h_slot_ids[i]);
+  }
+  if (batch == 0) return SSM_OK;
+  if (!x || !dt || !B || !C || !y) return fail(SSM_E_INVALID_ARG, "copy: NULL input or output");
+  st = check_io_align(H->io, x, dt, B, C, y, "copy");
+  if (st != SSM_OK) return st;
+  hipStream_t s = as_stream(stream);
+  const Dims &d = H->d;
+  const size_t nt = (size_t)batch * n_in;
+  st = check_finite(H, s, {{x, nt * d.H * d.P}, {dt, nt * d.H}, {B, nt * d.G * d.N},
+                           {C, nt * d.G * d.N}});
+  if (st != SSM_OK) return st;
+  const size_t es = io_size(H->io);
+  for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
+    const int n = std::min(kBatchPerLaunch, batch - i0);
+    CopyMeta m;
+    for (int i = 0; i < n; ++i) {
+      m.slot[i] = h_slot_ids[i0 + i];
+      m.src[i] = (int8_t)H->slots[h_slot_ids[i0 + i]].live;
+    }
+    const size_t off = (size_t)i0 * n_in;
+    CopyArgs a{};
+    a.x = (const char *)x + off * d.H * d.P * es;
+    a.dt = (const char *)dt + off * d.H * es;
+    a.B = (const char *)B + off * d.G * d.N * es;
+    a.C = (const char *)C + off * d.G * d.N * es;
+    a.y = (char *)y + off * d.H * d.P * es;
+    a.state = H->state;
+    a.copies = H->copies;
+    a.A = H->A;
+    a.D = H->D;
+    a.d = d;
+    a.n = n;
+    a.n_in = n_in;
+    a.n_in_max = H->n_in_max;
+    HIP_TRY(launch_copy(H->io, a, m, s));
+  }
+  for (int i = 0; i < batch; ++i) {
+    Slot &sl = H->slots[h_slot_ids[i]];
+    sl.pend = kCopyPend;
+    sl.pend_n = n_in;
+    H->cnt.state_bytes_read += H->state_bytes();
+    H->cnt.state_bytes_written += (size_t)n_in * H->state_bytes();
+  }
+  H->cnt.copy_steps++;
+  return SSM_OK;
+}
+
+ssm_status ssm_copy_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                           const int32_t *h_accepted) {
+  GET_HANDLE(H, h);
+  ssm_status st = check_slots(H, batch, h_slot_ids, "copy commit");
+  if (st != SSM_OK) return st;
+  if (batch > 0 && !h_accepted) return fail(SSM_E_INVALID_ARG, "copy commit: accepted is NULL");
+  for (int i = 0; i < batch; ++i) {
+    const Slot &sl = H->slots[h_slot_ids[i]];
+    if (sl.pend != kCopyPend)
+      return fail(SSM_E_LOG, "copy commit: slot %d has no copy step to commit", h_slot_ids[i]);
+    if (h_accepted[i] < 1 || h_accepted[i] > sl.pend_n)
+      return fail(SSM_E_LOG, "copy commit: slot %d accepted %d outside [1, %d]", h_slot_ids[i],
+                  h_accepted[i], sl.pend_n);
+  }
+  for (int i = 0; i < batch; ++i) {
+    Slot &sl = H->slots[h_slot_ids[i]];
+    sl.live = h_accepted[i] - 1;
+    sl.pos += h_accepted[i];
+    sl.pend = kNone;
+    sl.pend_n = 0;
+  }
+  return SSM_OK;
+}
+
+// -------------------------------------------------------- state operations
+ssm_status ssm_state_materialize(ssm_handle h, int32_t n, const int32_t *h_slots, void *stream) {
+  GET_HANDLE(H, h);
+  ssm_status st = check_slots(H, n, h_slots, "materialize");
+  if (st != SSM_OK) return st;
+  return materialize(H, n, h_slots, as_stream(stream));
+}
+
+ssm_status ssm_state_checkpoint(ssm_handle h, int32_t slot, float *d_dst, ssm_receipt *out,
+                                void *stream) {
+  GET_HANDLE(H, h);
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "checkpoint: bad slot %d", slot);
+  if (!d_dst || !out || !aligned(d_dst, 16))
+    return fail(SSM_E_INVALID_ARG, "checkpoint: NULL or misaligned destination, or NULL receipt");
+  if (H->slots[slot].pend != kNone)
+    return fail(SSM_E_LOG, "checkpoint: slot %d has a verify step awaiting commit", slot);
+  hipStream_t s = as_stream(stream);
+  const int32_t one = slot;
+  ssm_status st = materialize(H, 1, &one, s);
+  if (st != SSM_OK) return st;
+  HIP_TRY(launch_copy_f32(d_dst, H->slot_state(slot), H->state_bytes() / 4, s));
+  uint64_t sum = 0;
+  st = device_checksum(H, d_dst, s, &sum);
+  if (st != SSM_OK) return st;
+  const Slot &sl = H->slots[slot];
+  ssm_receipt r{};
+  r.stream_id = sl.stream_id;
+  r.model_rev = H->desc.model_rev;
+  r.code_rev = kCodeRev;
+  r.schema_version = H->desc.schema_version;
+  r.state_dtype = SSM_F32;
+  r.H = H->d.H;
+  r.P = H->d.P;
+  r.N = H->d.N;
+  r.G = H->d.G;
+  r.position = sl.pos;
+  r.chunk_seq = sl.chunk_seq;
+  r.checksum = sum;
+  *out = r;
+  H->cnt.checkpoints++;
+  H->cnt.state_bytes_read += H->state_bytes();
+  return SSM_OK;
+}
+
+ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
+                             const ssm_receipt *r, void *stream) {
+  GET_HANDLE(H, h);
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "restore: bad slot %d", slot);
+  if (!d_src || !r || !aligned(d_src, 16))
+    return fail(SSM_E_INVALID_ARG, "restore: NULL or misaligned source, or NULL receipt");
+  if (H->slots[slot].pend != kNone)
+    return fail(SSM_E_LOG, "restore: slot %d has a verify step awaiting commit", slot);
+  const char *bad = nullptr;
+  if (r->schema_version != H->desc.schema_version) bad = "schema version";
+  else if (r->state_dtype != SSM_F32) bad = "state dtype";
+  else if (r->H != H->d.H || r->P != H->d.P || r->N != H->d.N || r->G != H->d.G) bad = "dimensions";
+  else if (r->model_rev != H->desc.model_rev) bad = "model revision";
+  else if (r->code_rev != kCodeRev) bad = "code revision";
+  else if (r->position < 0) bad = "position";
+  if (bad) {
+    H->cnt.restores_rejected++;
+    return fail(SSM_E_SCHEMA, "restore: receipt %s does not match the handle", bad);
+  }
+  hipStream_t s = as_stream(stream);
+  uint64_t sum = 0;
+  ssm_status st = device_checksum(H, d_src, s, &sum);
+  if (st != SSM_OK) return st;
+  if (sum != r->checksum) {
+    H->cnt.restores_rejected++;
+    return fail(SSM_E_SCHEMA, "restore: checksum mismatch (state does not match its receipt)");
+  }
+  HIP_TRY(launch_copy_f32(H->slot_state(slot), d_src, H->state_bytes() / 4, s));
+  Slot &sl = H->slots[slot];
+  sl.pos = r->position;
+  sl.chunk_seq = r->chunk_seq;
+  sl.stream_id = r->stream_id;
+  sl.log_len = 0;
+  sl.live = -1;
+  sl.pend = kNone;
+  H->cnt.restores++;
+  H->cnt.state_bytes_written += H->state_bytes();
+  return SSM_OK;
+}
+
+ssm_status ssm_get_position(ssm_handle h, int32_t slot, int64_t *pos, uint64_t *chunk_seq) {
+  GET_HANDLE(H, h);
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "bad slot %d", slot);
+  if (pos) *pos = H->slots[slot].pos;
+  if (chunk_seq) *chunk_seq = H->slots[slot].chunk_seq;
+  return SSM_OK;
+}
+
+ssm_status ssm_get_log_state(ssm_handle h, int32_t slot, int32_t *log_len, int32_t *pending) {
+  GET_HANDLE(H, h);
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "bad slot %d", slot);
+  if (log_len) *log_len = H->slots[slot].log_len;
+  if (pending) *pending = H->slots[slot].pend;
+  return SSM_OK;
+}
+
+ssm_status ssm_get_counters(ssm_handle h, ssm_counters *out) {
+  GET_HANDLE(H, h);
+  if (!out) return fail(SSM_E_INVALID_ARG, "out is NULL");
+  *out = H->cnt;
+  return SSM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// ssm_internal.h -- launch-side declarations shared by the host runtime
+// (ssm_host.cpp) and the kernels (*.hip).  Library-internal: not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Batch entries per launch for decode / copy / replay.  Per-entry metadata
+// travels in the kernel arguments (no staging copies, nothing to allocate);
+// larger batches are split into several launches by the host.
+constexpr int kBatchPerLaunch = 256;
+// Segments (runs between resets) and checkpoints per scan launch.
+constexpr int kSegPerLaunch = 32;
+constexpr int kCkptPerLaunch = 64;
+// Rows of one workgroup's state tile and threads per workgroup.
+constexpr int kRows = 64;
+constexpr int kThreads = 256;
+// Largest supported state size N (one float4 per lane of a 32-lane row group).
+constexpr int kMaxN = 128;
+// Largest replay window and in-flight count.
+constexpr int kMaxW = 64;
+constexpr int kMaxInFlight = 16;
+
+enum IoType { kF32 = 0, kBF16 = 2 };
+
+struct Dims {
+  int H, P, N, G;
+  int PT;  // ceil(P / kRows): row tiles per head
+};
+
+// ---------------------------------------------------------------- decode
+struct DecodeMeta {
+  int32_t slot[kBatchPerLaunch];
+  uint8_t reset[kBatchPerLaunch];
+};
+struct DecodeArgs {
+  const void *x, *dt, *B, *C;  // this launch's first batch entry
+  void *y;
+  float *state;
+  const float *A, *D;
+  Dims d;
+  int n;  // entries in this launch
+};
+hipError_t launch_decode(int io, const DecodeArgs &a, const DecodeMeta &m, hipStream_t s);
+
+// ------------------------------------------------------------ copy baseline
+struct CopyMeta {
+  int32_t slot[kBatchPerLaunch];
+  int8_t src[kBatchPerLaunch];  // -1: read the slot state; k: read copy k
+};
+struct CopyArgs {
+  const void *x, *dt, *B, *C;  // [n, n_in, ...] for this launch
+  void *y;
+  const float *state;
+  float *copies;  // [S, n_in_max, H, P, N]
+  const float *A, *D;
+  Dims d;
+  int n, n_in, n_in_max;
+};
+hipError_t launch_copy(int io, const CopyArgs &a, const CopyMeta &m, hipStream_t s);
+
+// ------------------------------------------------------------------ replay
+struct ReplayMeta {
+  int32_t slot[kBatchPerLaunch];
+  uint8_t fold_len[kBatchPerLaunch];  // entries folded into the checkpoint first (0: none)
+  uint8_t base_len[kBatchPerLaunch];  // committed entries the in-flight tokens follow
+  uint8_t halves[kBatchPerLaunch];    // bit0: half read by the fold; bit1: half of the live log
+};
+struct ReplayArgs {
+  const void *x, *dt, *B, *C;  // [n, n_in, ...] for this launch
+  void *y;
+  float *state;                // checkpoints [S, H, P, N]
+  void *log;                   // [S][2][W] entries (see log_offsets)
+  float *bc;                   // scratch [n][G][W + n_in][n_in] inside the log buffer tail
+  const float *A, *D;
+  Dims d;
+  int n, n_in, W;
+};
+// Log layout: three arrays, each [S][2 halves][W entries][...] in the io dtype
+// (dt: [H], x: [H*P], B: [G*N]), then fp32 B.C scratch.
+struct LogLayout {
+  size_t dt_off, x_off, B_off, bc_off, total;  // byte offsets
+};
+LogLayout log_layout(int io, const Dims &d, int S, int W);
+hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const LogLayout &lay,
+                         hipStream_t s);
+
+// -------------------------------------------------------------------- scan
+struct ScanSeg {
+  int32_t t0, t1;   // token range [t0, t1) of the chunk
+  int32_t init;     // 1: start from the state buffer; 0: from zero
+  int32_t final;    // 0: drop; 1: write the state buffer; 2: write the workspace
+};
+struct ScanMeta {
+  ScanSeg seg[kSegPerLaunch];
+  int32_t ck_t[kCkptPerLaunch];    // token index (post-token state)
+  int32_t ck_idx[kCkptPerLaunch];  // destination index into ckpt_out
+};
+struct ScanArgs {
+  const void *x, *dt, *B, *C;
+  void *y;
+  float *state;      // the slot's [H, P, N]
+  float *workspace;  // [H, P, N] or null
+  float *ckpt_out;   // [n_ckpt, H, P, N]
+  const float *A, *D;
+  Dims d;
+  int n_seg, n_ck;
+};
+hipError_t launch_scan(int io, const ScanArgs &a, const ScanMeta &m, hipStream_t s);
+
+// --------------------------------------------------------------- state ops
+hipError_t launch_zero(float *dst, size_t n_floats, hipStream_t s);
+hipError_t launch_copy_f32(float *dst, const float *src, size_t n_floats, hipStream_t s);
+// sum_i w_i * (2*i + 1) mod 2^64 over the 32-bit words of src; *acc must be
+// zeroed first (launch_zero_u64).
+hipError_t launch_checksum(const float *src, size_t n_words, unsigned long long *acc,
+                           hipStream_t s);
+hipError_t launch_zero_u64(unsigned long long *p, int n, hipStream_t s);
+// Sets *flag to 1 if any of the n elements (io dtype) is not finite.
+hipError_t launch_finite_check(int io, const void *p, size_t n, unsigned int *flag,
+                               hipStream_t s);
+
+}  // namespace ssm

@@ -11,9 +11,9 @@ Distributions (same for every workload):
                                     bias, softplus or clamp of its own)
   A_h = -exp(u), u ~ U(0, ln 16)  so A_h lies in [-16, -1]
   D_h ~ N(0, 1)
-Decode and replay workloads start from a seeded fp32 state N(0, 0.02^2) and
-position 1000 (the pages leave the initial state open; this is the reading
-used).
+Decode and replay workloads start from a seeded fp32 state N(0, 0.02^2) at
+position 0, loaded as a learned initial state (the pages leave the initial
+state open; this is the reading used).
 
 Seeds: numpy PCG64 seeded from SeedSequence([20261202 + workload, tensor id,
 extra...]); each tensor (and each step of per-step tensors) has its own
@@ -140,7 +140,7 @@ def workload1(L=None):
 # ---------------------------------------------------------------------------
 # workload 2: batched decode, 256 requests, 64 steps, reset p = 0.02
 # ---------------------------------------------------------------------------
-W2 = dict(batch=256, H=128, P=64, N=128, G=1, steps=64, reset_p=0.02, pos0=1000)
+W2 = dict(batch=256, H=128, P=64, N=128, G=1, steps=64, reset_p=0.02)
 
 
 def decode_step_inputs(step, batch=256, H=128, P=64, N=128, G=1, workload=2):
@@ -158,8 +158,7 @@ def slot_permutation(workload, S, batch):
 # ---------------------------------------------------------------------------
 # workload 3: speculative verify, T = 4 drafts accepted i.i.d. p = 0.7
 # ---------------------------------------------------------------------------
-W3 = dict(batch=256, H=128, P=64, N=128, G=1, steps=128, T=4, p=0.7, windows=(8, 16, 32),
-          pos0=1000)
+W3 = dict(batch=256, H=128, P=64, N=128, G=1, steps=128, T=4, p=0.7, windows=(8, 16, 32))
 
 
 def spec_step_inputs(step, batch=256, n_in=5, H=128, P=64, N=128, G=1, workload=3):
@@ -256,3 +255,16 @@ def device_tokens(workload, L, H, P, N, G=1, seed_extra=0, device="cuda", dtype=
     B = torch.randn((L, G, N), generator=g, device=device, dtype=torch.float32) * s
     C = torch.randn((L, G, N), generator=g, device=device, dtype=torch.float32) * s
     return x.to(dtype), dt.to(dtype), B.to(dtype), C.to(dtype)
+
+
+def device_state(workload, S, H, P, N, std=0.02, device="cuda"):
+    """Seeded fp32 initial state N(0, std^2) drawn on the device ([S,H,P,N])."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((BASE_SEED + workload) * 7919 + 17)
+    return torch.randn((S, H, P, N), generator=g, device=device, dtype=torch.float32) * std
+
+
+def device_resets(workload, step, batch, p=0.02):
+    """Per-slot reset flags of one decode step (host u8[batch])."""
+    return (rng(workload, "reset", step).random(batch) < p).astype(np.uint8)

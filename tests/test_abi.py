@@ -1,0 +1,165 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad calls on the host before any device work
+(sequence numbers, slot ids, lifecycle misuse, incompatible receipts).
+
+Pointers passed here are never dereferenced: every call below fails (or, for
+an empty chunk, succeeds) before anything is enqueued.
+"""
+import ctypes
+import re
+
+import pytest
+
+ssm = pytest.importorskip("streaming_state_amd.ssm",
+                          reason="libssm_stream.so not built (python -m streaming_state_amd.build)")
+
+FAKE = ctypes.c_void_p(0x1000)  # a non-null device pointer that is never used
+
+
+def declared_functions():
+    text = open(ssm.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(ssm.lib(), n), f"{n} declared in ssm_stream.h but not exported"
+
+
+def _desc(H=4, P=8, N=16, G=1, io=ssm.SSM_F32):
+    return ssm.LayerDesc(H, P, N, G, io, 3, 77)
+
+
+def _create(S=4, desc=None, flags=0):
+    d = desc or _desc()
+    h = ctypes.c_int64(0)
+    rc = ssm.lib().ssm_create(ctypes.byref(d), S, FAKE, FAKE, FAKE, flags, ctypes.byref(h))
+    return rc, h.value
+
+
+def _err():
+    return ssm.lib().ssm_last_error().decode()
+
+
+def test_create_validates_layer():
+    for bad in (_desc(N=6), _desc(N=256), _desc(H=6, G=4), _desc(io=ssm.SSM_F16), _desc(P=0)):
+        rc, _ = _create(desc=bad)
+        assert rc == ssm.SSM_E_INVALID_ARG
+    rc, h = _create()
+    assert rc == ssm.SSM_OK and h > 0
+    assert ssm.lib().ssm_destroy(h) == ssm.SSM_OK
+
+
+def test_destroyed_handle_is_invalid_and_ids_not_reused():
+    rc, h = _create()
+    assert ssm.lib().ssm_destroy(h) == ssm.SSM_OK
+    assert ssm.lib().ssm_destroy(h) == ssm.SSM_E_INVALID_STATE
+    pos = ctypes.c_int64(0)
+    assert ssm.lib().ssm_get_position(h, 0, ctypes.byref(pos), None) == ssm.SSM_E_INVALID_STATE
+    rc, h2 = _create()
+    assert h2 != h
+    ssm.lib().ssm_destroy(h2)
+
+
+def _scan(h, slot, seq, L, reset=None, ckpt=None, ws=None):
+    rs = None if reset is None else (ctypes.c_uint8 * len(reset))(*reset)
+    ck = None if ckpt is None else (ctypes.c_int64 * len(ckpt))(*ckpt)
+    return ssm.lib().ssm_scan_chunk(h, slot, seq, L, FAKE, FAKE, FAKE, FAKE, rs, FAKE,
+                                    0 if ckpt is None else len(ckpt), ck,
+                                    FAKE if ckpt else None, ws, 0, None)
+
+
+def test_chunk_sequence_rules():
+    rc, h = _create()
+    lib = ssm.lib()
+    # an empty chunk is admitted and only advances the sequence number
+    assert _scan(h, 1, 0, 0) == ssm.SSM_OK
+    pos, seq = ctypes.c_int64(-1), ctypes.c_uint64(0)
+    lib.ssm_get_position(h, 1, ctypes.byref(pos), ctypes.byref(seq))
+    assert (pos.value, seq.value) == (0, 1)
+    # duplicate and reordered chunks are rejected with nothing changed
+    assert _scan(h, 1, 0, 5) == ssm.SSM_E_SEQUENCE
+    assert "duplicate" in _err()
+    assert _scan(h, 1, 2, 5) == ssm.SSM_E_SEQUENCE
+    assert _scan(h, 1, 7, 0) == ssm.SSM_E_SEQUENCE
+    lib.ssm_get_position(h, 1, ctypes.byref(pos), ctypes.byref(seq))
+    assert (pos.value, seq.value) == (0, 1)
+    c = ssm.Counters()
+    lib.ssm_get_counters(h, ctypes.byref(c))
+    assert c.chunks_admitted == 1 and c.chunks_rejected == 3
+    lib.ssm_destroy(h)
+
+
+def test_scan_argument_checks():
+    rc, h = _create()
+    assert _scan(h, 9, 0, 4) == ssm.SSM_E_INVALID_ARG             # slot out of range
+    assert _scan(h, 0, 0, -1) == ssm.SSM_E_INVALID_ARG            # negative length
+    assert _scan(h, 0, 0, 4, ckpt=[2, 2]) == ssm.SSM_E_INVALID_ARG  # not increasing
+    assert _scan(h, 0, 0, 4, ckpt=[4]) == ssm.SSM_E_INVALID_ARG     # outside [0, L)
+    # carries state in and resets later: needs the workspace
+    assert _scan(h, 0, 0, 4, reset=[0, 0, 1, 0]) == ssm.SSM_E_INVALID_ARG
+    assert "workspace" in _err()
+    ssm.lib().ssm_destroy(h)
+
+
+def test_batch_slot_checks():
+    rc, h = _create(S=4)
+    lib = ssm.lib()
+    ids = (ctypes.c_int32 * 3)(0, 2, 0)
+    assert lib.ssm_decode_step(h, 3, ids, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == \
+        ssm.SSM_E_INVALID_ARG
+    assert "repeated" in _err()
+    ids = (ctypes.c_int32 * 2)(0, 4)
+    assert lib.ssm_decode_step(h, 2, ids, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == \
+        ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_state_reset(h, 2, ids, None) == ssm.SSM_E_INVALID_ARG
+    lib.ssm_destroy(h)
+
+
+def test_replay_and_copy_bookkeeping_misuse():
+    rc, h = _create(S=4)
+    lib = ssm.lib()
+    ids = (ctypes.c_int32 * 1)(1)
+    acc = (ctypes.c_int32 * 1)(1)
+    # no log attached / nothing to commit
+    assert lib.ssm_replay_step(h, 1, ids, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ssm.SSM_E_LOG
+    assert lib.ssm_replay_commit(h, 1, ids, acc) == ssm.SSM_E_LOG
+    assert lib.ssm_copy_commit(h, 1, ids, acc) == ssm.SSM_E_LOG
+    d = _desc()
+    nb = lib.ssm_replay_log_bytes(ctypes.byref(d), 4, 8)
+    assert nb > 0
+    assert lib.ssm_replay_log_bytes(ctypes.byref(d), 4, 65) == 0  # window above the limit
+    assert lib.ssm_replay_attach(h, 8, FAKE, nb - 1) == ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_replay_attach(h, 8, FAKE, nb) == ssm.SSM_OK
+    assert lib.ssm_replay_step(h, 1, ids, 9, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        ssm.SSM_E_INVALID_ARG  # n_in above W
+    assert lib.ssm_copy_step(h, 1, ids, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ssm.SSM_E_LOG
+    lib.ssm_destroy(h)
+
+
+def test_restore_rejects_incompatible_receipts():
+    rc, h = _create(desc=_desc())
+    lib = ssm.lib()
+    good = dict(stream_id=5, model_rev=77, code_rev=ssm.code_rev(), schema_version=3,
+                state_dtype=0, H=4, P=8, N=16, G=1, position=10, chunk_seq=2, checksum=0)
+    for field, value in (("schema_version", 4), ("model_rev", 78), ("code_rev", 999),
+                         ("N", 32), ("H", 2), ("state_dtype", 2)):
+        r = ssm.Receipt.from_dict(dict(good, **{field: value}))
+        assert lib.ssm_state_restore(h, 0, FAKE, ctypes.byref(r), None) == ssm.SSM_E_SCHEMA, field
+    c = ssm.Counters()
+    lib.ssm_get_counters(h, ctypes.byref(c))
+    assert c.restores_rejected == 6
+    lib.ssm_destroy(h)
+
+
+def test_size_queries():
+    lib = ssm.lib()
+    d = _desc(H=128, P=64, N=128)
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 128 * 64 * 128 * 4
+    assert lib.ssm_copy_buffer_bytes(ctypes.byref(d), 256, 5) == 256 * 5 * 4 * 1024 * 1024
+    # the log holds two halves of W entries of dt[H], x[H,P], B[G,N] per slot
+    entry = (128 + 128 * 64 + 128) * 4
+    assert lib.ssm_replay_log_bytes(ctypes.byref(d), 256, 16) >= 256 * 2 * 16 * entry

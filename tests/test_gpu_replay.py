@@ -1,0 +1,117 @@
+"""Replay and copy-baseline parity: ReplaySSM verify (checkpoint + log, fused
+fold when the log fills) and the copy-state-per-draft baseline, through the C
+ABI, vs the oracle's step-by-step recurrence with rollback.  Flush counts and
+positions must match the oracle's schedule exactly."""
+import numpy as np
+import pytest
+
+import oracle
+from streaming_state_amd import inputs
+from tests.gpu_helpers import F32_TOL, assert_close, bf16_dev, bf16_tol, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from streaming_state_amd import ssm as m
+    return m
+
+
+@pytest.mark.parametrize("W,n_in,H,P,N,G,io", [
+    (8, 5, 2, 8, 16, 1, "f32"),
+    (16, 5, 3, 40, 20, 1, "f32"),
+    (32, 5, 4, 72, 128, 2, "f32"),
+    (8, 1, 2, 64, 128, 1, "f32"),   # one token per step: the plain-decode case
+    (16, 5, 2, 64, 128, 1, "bf16"),
+    (5, 5, 2, 16, 32, 1, "f32"),    # every step flushes a full window
+])
+def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io):
+    S, b, steps = 6, 4, 40
+    say("replay small", W, n_in, H, P, N, G, io)
+    A, D = inputs.params(40, H)
+    st0 = np.random.default_rng(W).standard_normal((S, H, P, N)).astype(np.float32) * 0.1
+    rep = ssm.StreamState(H, P, N, S, to_dev(A), to_dev(D), G=G, io_dtype=io)
+    cop = ssm.StreamState(H, P, N, S, to_dev(A), to_dev(D), G=G, io_dtype=io)
+    rep.init(np.arange(S), to_dev(st0))
+    cop.init(np.arange(S), to_dev(st0))
+    rep.replay_attach(W)
+    cop.copy_attach(n_in)
+    slots = np.array([5, 1, 2, 0], np.int32)
+    ref_state = st0.astype(np.float64).copy()
+    ref_pos = np.zeros(S, np.int64)
+    acc = inputs.acceptances(steps, b, T=n_in - 1, p=0.7) if n_in > 1 else \
+        np.ones((steps, b), np.int32)
+    sched = oracle.replay_schedule(acc, W, n_in)
+    for s in range(steps):
+        x, dt, B, C = inputs.spec_step_inputs(s, batch=b, n_in=n_in, H=H, P=P, N=N, G=G,
+                                              workload=40)
+        if io == "bf16":
+            bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
+            x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
+            dev = [bf16_dev(a) for a in bits]
+        else:
+            dev = [to_dev(a) for a in (x, dt, B, C)]
+        y_rep = rep.replay_step(slots, *dev)
+        y_cop = cop.copy_step(slots, *dev)
+        ref_y = oracle.spec_step(ref_state, ref_pos, slots, x, dt, B, C, A, D, acc[s])
+        torch.cuda.synchronize()
+        tol = bf16_tol(ref_y) if io == "bf16" else F32_TOL
+        assert_close(host(y_rep), ref_y, what=f"replay y step {s}", **tol)
+        assert_close(host(y_cop), ref_y, what=f"copy y step {s}", **tol)
+        rep.replay_commit(slots, acc[s])
+        cop.copy_commit(slots, acc[s])
+        for i, sl in enumerate(slots):
+            assert rep.log_state(int(sl))[0] == sched["len_before"][s, i] + acc[s, i]
+    c = rep.counters()
+    assert c["replay_flushes"] == int(sched["flushes"].sum())
+    rep.materialize(slots)
+    cop.materialize(slots)
+    torch.cuda.synchronize()
+    stol = bf16_tol(ref_state) if io == "bf16" else F32_TOL
+    assert_close(host(rep.state), ref_state, what="replay state", **stol)
+    assert_close(host(cop.state), ref_state, what="copy state", **stol)
+    for sl in range(S):
+        assert rep.position(sl)[0] == ref_pos[sl] == cop.position(sl)[0]
+    rep.destroy()
+    cop.destroy()
+
+
+@pytest.mark.parametrize("W", [8, 16, 32])
+def test_replay_workload3_full_batch(ssm, W):
+    """B=256, H=128, P=64, N=128, T=4 drafts accepted with p=0.7; the oracle
+    follows 6 sampled slots over 24 steps."""
+    Wc = inputs.W3
+    B_, H, P, N, G = Wc["batch"], Wc["H"], Wc["P"], Wc["N"], Wc["G"]
+    n_in, steps = Wc["T"] + 1, 24
+    say("replay workload3", W)
+    A, D = inputs.params(3, H)
+    init = inputs.device_state(3, B_, H, P, N)
+    h = ssm.StreamState(H, P, N, B_, to_dev(A), to_dev(D), G=G)
+    h.init(np.arange(B_), init)
+    h.replay_attach(W)
+    slots = np.arange(B_, dtype=np.int32)
+    acc = inputs.acceptances(Wc["steps"], B_, T=Wc["T"], p=Wc["p"])[:steps]
+    sched = oracle.replay_schedule(acc, W, n_in)
+    sample = np.array([0, 3, 99, 128, 200, 255])
+    idx = torch.as_tensor(sample).long().cuda()
+    ref_state = host(init[idx])
+    ref_pos = np.zeros(len(sample), np.int64)
+    for s in range(steps):
+        x, dt, B, C = inputs.device_tokens(3, B_ * n_in, H, P, N, G, seed_extra=s)
+        x, dt = x.view(B_, n_in, H, P), dt.view(B_, n_in, H)
+        B, C = B.view(B_, n_in, G, N), C.view(B_, n_in, G, N)
+        y = h.replay_step(slots, x, dt, B, C)
+        ref_y = oracle.spec_step(ref_state, ref_pos, np.arange(len(sample)), host(x[idx]),
+                                 host(dt[idx]), host(B[idx]), host(C[idx]), A, D,
+                                 acc[s][sample], n_threads=None)
+        assert_close(host(y[idx]), ref_y, what=f"y step {s}", **F32_TOL)
+        h.replay_commit(slots, acc[s])
+    assert h.counters()["replay_flushes"] == int(sched["flushes"].sum())
+    h.materialize(slots)
+    assert_close(host(h.state[idx]), ref_state, what="state", **F32_TOL)
+    h.destroy()

@@ -1,0 +1,172 @@
+"""Chunk-scan parity: the HIP scan through the C ABI vs the fp64 oracle, over
+every chunking of the tiny fixture, the Mamba-130M-shaped layer streamed in
+chunks, ragged shapes with resets and checkpoints, and the 65,536-token packed
+bf16 prefill (sampled heads)."""
+import numpy as np
+import pytest
+
+import oracle
+from streaming_state_amd import inputs
+from tests.gpu_helpers import F32_TOL, assert_close, bf16_dev, bf16_tol, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from streaming_state_amd import ssm as m
+    return m
+
+
+def _stream_chunks(h, slot, sizes, dev, reset=None):
+    """Scan dev tensors chunk by chunk; return concatenated y."""
+    ys, t0 = [], 0
+    for seq, s in enumerate(sizes):
+        sl = slice(t0, t0 + s)
+        y = h.scan_chunk(slot, seq, dev[0][sl], dev[1][sl], dev[2][sl], dev[3][sl],
+                         reset=None if reset is None else reset[sl])
+        ys.append(y)
+        t0 += s
+    return torch.cat(ys) if ys else None
+
+
+def test_workload0_every_chunking(ssm):
+    w = inputs.workload0()
+    L, H, P, N = w["L"], w["H"], w["P"], w["N"]
+    reset = np.zeros(L, np.uint8)
+    reset[w["reset_at"]] = 1
+    ref = oracle.scan(w["x"], w["dt"], w["B"], w["C"], w["A"], w["D"], reset=reset)
+    dev = [to_dev(w[k]) for k in ("x", "dt", "B", "C")]
+    for pi, sizes in enumerate(inputs.partitions0(L)):
+        say("workload0 partition", pi, sizes)
+        h = ssm.StreamState(H, P, N, 2, to_dev(w["A"]), to_dev(w["D"]))
+        h.reset([0, 1])
+        y = _stream_chunks(h, 1, sizes, dev, reset)
+        torch.cuda.synchronize()
+        assert_close(host(y), ref["y"], what=f"y {sizes}", **F32_TOL)
+        assert_close(host(h.state[1]), ref["state"], what=f"state {sizes}", **F32_TOL)
+        assert h.position(1) == (ref["pos"], len(sizes))
+        assert float(h.state[0].abs().max()) == 0.0  # the other slot is untouched
+        h.destroy()
+
+
+def test_workload0_reset_separation(ssm):
+    """Prefix, reset, then B equals B from a fresh state; without the reset it
+    differs (inequality control near the boundary)."""
+    w = inputs.workload0()
+    L, H, P, N, k = w["L"], w["H"], w["P"], w["N"], w["reset_at"]
+    dev = [to_dev(w[n]) for n in ("x", "dt", "B", "C")]
+    h = ssm.StreamState(H, P, N, 3, to_dev(w["A"]), to_dev(w["D"]))
+    h.reset([0, 1, 2])
+    say("workload0 reset separation")
+    reset = np.zeros(L, np.uint8)
+    reset[k] = 1
+    y_r = h.scan_chunk(0, 0, *dev, reset=reset)
+    y_f = h.scan_chunk(1, 0, *[d[k:] for d in dev])
+    y_n = h.scan_chunk(2, 0, *dev)
+    torch.cuda.synchronize()
+    assert_close(host(y_r[k:]), host(y_f), what="reset vs fresh", rtol=1e-6, atol=1e-6)
+    assert_close(host(h.state[0]), host(h.state[1]), what="state", rtol=1e-6, atol=1e-6)
+    assert np.abs(host(y_r[k]) - host(y_n[k])).max() > 1e-5
+    assert h.position(0)[0] == L - k
+
+
+@pytest.mark.parametrize("chunk", [None, 256, 64, 17, 1])
+def test_workload1_streaming(ssm, chunk):
+    """Mamba-130M-shaped layer (H=24, P=64, N=128, L=2048, fp32): full scan and
+    chunked streaming with the state carried across chunks."""
+    w = inputs.workload1()
+    L, H, P, N = w["L"], w["H"], w["P"], w["N"]
+    say("workload1 chunk", chunk)
+    ref = oracle.scan(w["x"], w["dt"], w["B"], w["C"], w["A"], w["D"], n_threads=None)
+    dev = [to_dev(w[k]) for k in ("x", "dt", "B", "C")]
+    h = ssm.StreamState(H, P, N, 1, to_dev(w["A"]), to_dev(w["D"]))
+    h.reset([0])
+    sizes = [L] if chunk is None else [chunk] * (L // chunk) + ([L % chunk] if L % chunk else [])
+    y = _stream_chunks(h, 0, sizes, dev)
+    torch.cuda.synchronize()
+    assert_close(host(y), ref["y"], what="y", **F32_TOL)
+    assert_close(host(h.state[0]), ref["state"], what="state", **F32_TOL)
+    assert h.position(0) == (L, len(sizes))
+
+
+@pytest.mark.parametrize("H,P,N,G,io,L", [
+    (3, 40, 20, 1, "f32", 97),
+    (4, 72, 128, 2, "f32", 130),
+    (2, 64, 128, 1, "bf16", 301),
+    (4, 16, 64, 4, "bf16", 77),
+])
+def test_ragged_resets_checkpoints(ssm, H, P, N, G, io, L):
+    say("scan ragged", H, P, N, G, io, L)
+    r = np.random.default_rng(L)
+    x, dt, B, C = inputs.tokens(30, L, H, P, N, G)
+    A, D = inputs.params(30, H)
+    if io == "bf16":
+        bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
+        x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
+        dev = [bf16_dev(a) for a in bits]
+    else:
+        dev = [to_dev(a) for a in (x, dt, B, C)]
+    st0 = r.standard_normal((H, P, N)).astype(np.float32) * 0.05
+    reset = np.zeros(L, np.uint8)
+    reset[[L // 3, L // 3 + 1, (2 * L) // 3]] = 1
+    ck = sorted({0, L // 3 - 1, L // 3, L // 2, L - 1})
+    ref = oracle.scan(x, dt, B, C, A, D, state=st0, pos=5, reset=reset, ckpt_at=ck)
+    h = ssm.StreamState(H, P, N, 2, to_dev(A), to_dev(D), G=G, io_dtype=io)
+    h.init([1], to_dev(st0[None]))
+    y, cko = h.scan_chunk(1, 0, *dev, reset=reset, ckpt_at=ck)
+    torch.cuda.synchronize()
+    tol = (lambda a: bf16_tol(a)) if io == "bf16" else (lambda a: F32_TOL)
+    assert_close(host(y), ref["y"], what="y", **tol(ref["y"]))
+    assert_close(host(cko), ref["ckpt"], what="checkpoints", **tol(ref["ckpt"]))
+    assert_close(host(h.state[1]), ref["state"], what="carry-out", **tol(ref["state"]))
+    # the last reset fixes the position: tokens after it
+    assert h.position(1) == (ref["pos"], 1) and ref["pos"] == L - (2 * L) // 3
+
+
+def test_empty_chunk_is_neutral(ssm):
+    w = inputs.workload0()
+    H, P, N = w["H"], w["P"], w["N"]
+    say("empty chunk")
+    dev = [to_dev(w[k]) for k in ("x", "dt", "B", "C")]
+    h = ssm.StreamState(H, P, N, 1, to_dev(w["A"]), to_dev(w["D"]))
+    h.reset([0])
+    h.scan_chunk(0, 0, *[d[:10] for d in dev])
+    before = h.state.clone()
+    e = [d[:0] for d in dev]
+    y = h.scan_chunk(0, 1, *e)
+    torch.cuda.synchronize()
+    assert y.shape[0] == 0
+    assert torch.equal(before, h.state)
+    assert h.position(0) == (10, 2)
+
+
+def test_workload4_packed_prefill_sampled_heads(ssm):
+    """8 packed sequences, 65,536 tokens, H=128, P=64, N=128, bf16 inputs, fp32
+    state, reset at every sequence start, final states emitted as checkpoints.
+    The oracle runs three sampled heads over all tokens."""
+    W = inputs.W4
+    L, H, P, N, G = W["L"], W["H"], W["P"], W["N"], W["G"]
+    lengths = inputs.sequence_lengths()
+    reset, cu, ends = inputs.packed_layout(lengths)
+    say("workload4", lengths.tolist())
+    d = inputs.device_prefill(L, H, P, N, G)
+    h = ssm.StreamState(H, P, N, 1, d["A"], d["D"], G=G, io_dtype="bf16")
+    h.reset([0])
+    y, cko = h.scan_chunk(0, 0, d["x"], d["dt"], d["B"], d["C"], reset=reset, ckpt_at=ends)
+    torch.cuda.synchronize()
+    heads = [0, 61, 127]
+    A, D = inputs.params(4, H)
+    hs = torch.as_tensor(heads).long().cuda()
+    ref = oracle.scan(host(d["x"][:, hs]), host(d["dt"][:, hs]), host(d["B"]), host(d["C"]),
+                      A[heads], D[heads], reset=reset, ckpt_at=ends, n_threads=None)
+    ys = host(y[:, hs])
+    assert_close(ys, ref["y"], what="y", **bf16_tol(ref["y"]))
+    ck = host(cko[:, hs])
+    assert_close(ck, ref["ckpt"], what="checkpoints", **bf16_tol(ref["ckpt"]))
+    assert_close(host(h.state[0][hs]), ref["state"], what="carry-out", **bf16_tol(ref["state"]))
+    assert h.position(0)[0] == lengths[-1]
