@@ -17,12 +17,15 @@ typedef uint16_t bf16_t;
 __device__ __forceinline__ float bf16_to_f(bf16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even with the hardware conversion (v_cvt_pk_bf16_f32 on
+// gfx950, two values per instruction); NaN stays NaN.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16_t f_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const bf16x2_hw v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Io;
@@ -46,8 +49,8 @@ template <> struct Io<bf16_t> {
   static __device__ __forceinline__ void st(bf16_t *p, float v) { *p = f_to_bf16(v); }
   static __device__ __forceinline__ void st4(bf16_t *p, float4 v) {
     uint2 r;
-    r.x = (uint32_t)f_to_bf16(v.x) | ((uint32_t)f_to_bf16(v.y) << 16);
-    r.y = (uint32_t)f_to_bf16(v.z) | ((uint32_t)f_to_bf16(v.w) << 16);
+    r.x = pack2_bf16(v.x, v.y);
+    r.y = pack2_bf16(v.z, v.w);
     *reinterpret_cast<uint2 *>(p) = r;
   }
 };

@@ -15,7 +15,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "../../include/ssm_stream.h"
+#include "ssm_stream.h"
 #include "ssm_internal.h"
 
 using namespace ssm;
@@ -398,6 +398,9 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
   if (!x || !dt || !B || !C || !y) return fail(SSM_E_INVALID_ARG, "scan: NULL input or output");
   st = check_io_align(H->io, x, dt, B, C, y, "scan");
   if (st != SSM_OK) return st;
+  const bool ssd = ssd_supported(H->io, H->d);
+  if (ssd && (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16)))
+    return fail(SSM_E_INVALID_ARG, "scan: bf16 x, B and C must be 16-byte aligned");
   if ((n_ckpt > 0 && !aligned(d_ckpt_out, 16)) || !aligned(d_workspace, 16))
     return fail(SSM_E_INVALID_ARG, "scan: checkpoint and workspace buffers must be 16-byte aligned");
   // segments: runs between resets
@@ -429,6 +432,10 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
     const int ns = (int)std::min<size_t>(kSegPerLaunch, segs.size() - i0);
     ScanMeta m{};
     for (int i = 0; i < ns; ++i) m.seg[i] = segs[i0 + i];
+    if (ssd)  // longest segments first: one workgroup per (segment, head) runs it in order
+      std::stable_sort(m.seg, m.seg + ns, [](const ScanSeg &a, const ScanSeg &b) {
+        return a.t1 - a.t0 > b.t1 - b.t0;
+      });
     const int32_t lo = segs[i0].t0, hi = segs[i0 + ns - 1].t1;
     int nck = 0;
     for (int i = 0; i < n_ckpt; ++i)
@@ -451,7 +458,10 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
     a.d = H->d;
     a.n_seg = ns;
     a.n_ck = nck;
-    HIP_TRY(launch_scan(H->io, a, m, s));
+    if (ssd)
+      HIP_TRY(launch_scan_ssd(a, m, s));
+    else
+      HIP_TRY(launch_scan(H->io, a, m, s));
   }
   if (need_ws)
     HIP_TRY(launch_copy_f32(H->slot_state(slot), (const float *)d_workspace,

@@ -110,6 +110,10 @@ struct ScanArgs {
   int n_seg, n_ck;
 };
 hipError_t launch_scan(int io, const ScanArgs &a, const ScanMeta &m, hipStream_t s);
+// SSD/MFMA form of the scan: bf16 inputs with P = 64 and N = 128 (x, B, C
+// 16-byte aligned).
+bool ssd_supported(int io, const Dims &d);
+hipError_t launch_scan_ssd(const ScanArgs &a, const ScanMeta &m, hipStream_t s);
 
 // --------------------------------------------------------------- state ops
 hipError_t launch_zero(float *dst, size_t n_floats, hipStream_t s);

@@ -170,3 +170,33 @@ def test_workload4_packed_prefill_sampled_heads(ssm):
     assert_close(ck, ref["ckpt"], what="checkpoints", **bf16_tol(ref["ckpt"]))
     assert_close(host(h.state[0][hs]), ref["state"], what="carry-out", **bf16_tol(ref["state"]))
     assert h.position(0)[0] == lengths[-1]
+
+
+@pytest.mark.parametrize("sizes", [[700], [1] * 20 + [680], [37] * 18 + [34], [64, 129, 3, 504],
+                                   [0, 300, 0, 400]])
+def test_bf16_mfma_path_chunked_with_reset(ssm, sizes):
+    """bf16, P=64, N=128 (the MFMA path): streamed in chunks with the state
+    carried across, a reset at t=300 inside a chunk, checkpoints mid-chunk."""
+    H, P, N, L = 4, 64, 128, 700
+    say("bf16 chunked", sizes[:4])
+    x, dt, B, C = inputs.tokens(31, L, H, P, N, 1)
+    A, D = inputs.params(31, H)
+    bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
+    x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
+    dev = [bf16_dev(a) for a in bits]
+    reset = np.zeros(L, np.uint8)
+    reset[300] = 1
+    st0 = np.random.default_rng(5).standard_normal((H, P, N)).astype(np.float32) * 0.05
+    ref = oracle.scan(x, dt, B, C, A, D, state=st0, reset=reset)
+    h = ssm.StreamState(H, P, N, 1, to_dev(A), to_dev(D), io_dtype="bf16")
+    h.init([0], to_dev(st0[None]))
+    ys, t0 = [], 0
+    for q, s in enumerate(sizes):
+        sl = slice(t0, t0 + s)
+        ys.append(h.scan_chunk(0, q, *[d_[sl] for d_ in dev], reset=reset[sl]))
+        t0 += s
+    torch.cuda.synchronize()
+    y = torch.cat(ys)
+    assert_close(host(y), ref["y"], what="y", **bf16_tol(ref["y"]))
+    assert_close(host(h.state[0]), ref["state"], what="state", **bf16_tol(ref["state"]))
+    assert h.position(0) == (L - 300, len(sizes))
