@@ -56,28 +56,34 @@ template <> struct Io<bf16_t> {
 };
 
 // -------------------------------------------------------- state-tile layout
-// A workgroup of 256 threads (4 waves) owns a 64-row x N tile of one head's
+// A group of 256 threads (4 waves) owns an (8*R)-row x N tile of one head's
 // fp32 state.  Lane l of wave w holds float4 column c = l & 31 (state entries
-// n = 4c..4c+3) of rows r_i = 8*i + 2*w + (l >> 5), i = 0..7.  One wave-wide
+// n = 4c..4c+3) of rows r_i = 8*i + 2*w + (l >> 5), i = 0..R-1.  One wave-wide
 // load instruction therefore covers two adjacent rows (2 * 512 B contiguous
 // at N = 128).
-struct Tile {
+template <int R>
+struct TileR {
+  static constexpr int kRowsPerTile = 8 * R;
   int lane, wave, c, rsub;
-  __device__ __forceinline__ Tile() {
+  __device__ __forceinline__ TileR() {
     lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
+    wave = (threadIdx.x >> 6) & 3;  // wave within the tile's 256 threads
     c = lane & 31;
     rsub = lane >> 5;
   }
   __device__ __forceinline__ int row(int i) const { return 8 * i + 2 * wave + rsub; }
-  // Row (within the tile) whose total this lane holds after reduce8().
+  // Row (within the tile) whose total this lane holds after reduce_rows<R>().
   __device__ __forceinline__ int reduced_row() const {
-    int r = ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
-    return row(r);
+    const int i = R == 8 ? ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1)
+                         : ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+    return row(i);
   }
-  // One lane of each group of four that hold the same reduced total.
-  __device__ __forceinline__ bool reduced_writer() const { return (lane & 3) == 0; }
+  // One lane of each group that holds the same reduced total.
+  __device__ __forceinline__ bool reduced_writer() const {
+    return R == 8 ? (lane & 3) == 0 : (lane & 7) == 0;
+  }
 };
+typedef TileR<8> Tile;
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
@@ -105,6 +111,26 @@ __device__ __forceinline__ float reduce8(const float v[8], int lane) {
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 1);
   return s;
+}
+// Four-row variant: after two halving steps each lane holds one row; the
+// remaining three exchanges finish the 32-lane sum.
+__device__ __forceinline__ float reduce4(const float v[4], int lane) {
+  const int b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1;
+  float s2[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) s2[i] = halve(v[i], v[i + 2], b4, 16);
+  float s = halve(s2[0], s2[1], b3, 8);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  return s;
+}
+template <int R> __device__ __forceinline__ float reduce_rows(const float v[R], int lane);
+template <> __device__ __forceinline__ float reduce_rows<8>(const float v[8], int lane) {
+  return reduce8(v, lane);
+}
+template <> __device__ __forceinline__ float reduce_rows<4>(const float v[4], int lane) {
+  return reduce4(v, lane);
 }
 
 // Streaming (nontemporal) 128-bit state accesses: the state is touched once

@@ -505,9 +505,11 @@ ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
   for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
     const int n = std::min(kBatchPerLaunch, batch - i0);
     DecodeMeta m;
-    for (int i = 0; i < n; ++i) {
-      m.slot[i] = h_slot_ids[i0 + i];
-      m.reset[i] = h_reset ? (h_reset[i0 + i] != 0) : 0;
+    for (int k = 0; k < n; ++k) {
+      const int i = k;
+      m.slot[k] = h_slot_ids[i0 + i];
+      m.ent[k] = (uint16_t)i;
+      m.reset[k] = h_reset ? (h_reset[i0 + i] != 0) : 0;
     }
     DecodeArgs a{};
     a.x = (const char *)x + (size_t)i0 * d.H * d.P * es;

@@ -33,7 +33,8 @@ struct Dims {
 
 // ---------------------------------------------------------------- decode
 struct DecodeMeta {
-  int32_t slot[kBatchPerLaunch];
+  int32_t slot[kBatchPerLaunch];   // in ascending slot order (state locality)
+  uint16_t ent[kBatchPerLaunch];   // batch entry of each slot (rows of x, dt, B, C, y)
   uint8_t reset[kBatchPerLaunch];
 };
 struct DecodeArgs {

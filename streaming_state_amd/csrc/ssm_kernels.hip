@@ -16,26 +16,38 @@ static __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 
 // ===========================================================================
 // decode: h <- exp(dt A) h + dt x B^T ; y = h C + D x, one token per slot
 // ===========================================================================
-template <typename T>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, DecodeMeta m) {
-  const Tile tl;
+// Decode tiles: R float4 rows per thread (a 256-thread tile covers 8R state
+// rows of one head) and kDecodeTiles consecutive tiles of one slot per
+// workgroup.  On MI355X an in-place read-modify-write sweep is fastest with
+// 16 KiB or 128 KiB per workgroup and slowest with 32-64 KiB.
+constexpr int kDecodeR = 4;
+constexpr int kDecodeTiles = 2;
+
+template <typename T, int R, int TW>
+__global__ __launch_bounds__(kThreads *TW) void decode_kernel(DecodeArgs a, DecodeMeta m) {
+  const TileR<R> tl;
   const Dims d = a.d;
-  int bid = blockIdx.x;
-  const int pt = bid % d.PT;
-  bid /= d.PT;
-  const int h = bid % d.H;
-  const int e = bid / d.H;
-  const int slot = m.slot[e];
-  const bool rst = m.reset[e] != 0;
+  constexpr int kTileRows = 8 * R;
+  const int pt_n = (d.P + kTileRows - 1) / kTileRows;
+  const int tiles_per_entry = d.H * pt_n;
+  const int groups = (tiles_per_entry + TW - 1) / TW;
+  const int k = blockIdx.x / groups;
+  const int tile = (blockIdx.x % groups) * TW + (int)(threadIdx.x / kThreads);
+  if (tile >= tiles_per_entry) return;  // no barriers below: tiles are independent
+  const int pt = tile % pt_n;
+  const int h = tile / pt_n;
+  const int slot = m.slot[k];
+  const int e = m.ent[k];
+  const bool rst = m.reset[k] != 0;
   const int g = h / (d.H / d.G);
-  const int prow0 = pt * kRows;
+  const int prow0 = pt * kTileRows;
   const bool colok = 4 * tl.c < d.N;
 
   float *st = a.state + (((size_t)slot * d.H + h) * d.P + prow0) * d.N + 4 * tl.c;
   // state first: the only large read, issued before anything else
-  float4 hv[8];
+  float4 hv[R];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < R; ++i) {
     const bool ok = colok && (prow0 + tl.row(i) < d.P) && !rst;
     hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * d.N) : zero4();
   }
@@ -48,27 +60,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, DecodeMe
     Bv = Io<T>::ld4((const T *)a.B + ((size_t)e * d.G + g) * d.N + 4 * tl.c);
     Cv = Io<T>::ld4((const T *)a.C + ((size_t)e * d.G + g) * d.N + 4 * tl.c);
   }
-  float part[8];
+  float part[R];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < R; ++i) {
     const bool rowok = prow0 + tl.row(i) < d.P;
     const float u = rowok ? dt * Io<T>::ld(x + tl.row(i)) : 0.f;
     hv[i] = fma4(dA, hv[i], u, Bv);
     if (rowok && colok) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
     part[i] = dot4(hv[i], Cv);
   }
-  const float yv = reduce8(part, tl.lane);
+  const float yv = reduce_rows<R>(part, tl.lane);
   const int r = tl.reduced_row();
   if (tl.reduced_writer() && prow0 + r < d.P)
     Io<T>::st((T *)a.y + ((size_t)e * d.H + h) * d.P + prow0 + r, yv + Dh * Io<T>::ld(x + r));
 }
 
 hipError_t launch_decode(int io, const DecodeArgs &a, const DecodeMeta &m, hipStream_t s) {
-  dim3 grid(a.n * a.d.H * a.d.PT), block(kThreads);
+  constexpr int kTileRows = 8 * kDecodeR;
+  const int tiles = a.d.H * ((a.d.P + kTileRows - 1) / kTileRows);
+  dim3 grid(a.n * ((tiles + kDecodeTiles - 1) / kDecodeTiles)), block(kThreads * kDecodeTiles);
   if (io == kBF16)
-    hipLaunchKernelGGL(decode_kernel<bf16_t>, grid, block, 0, s, a, m);
+    hipLaunchKernelGGL((decode_kernel<bf16_t, kDecodeR, kDecodeTiles>), grid, block, 0, s, a, m);
   else
-    hipLaunchKernelGGL(decode_kernel<float>, grid, block, 0, s, a, m);
+    hipLaunchKernelGGL((decode_kernel<float, kDecodeR, kDecodeTiles>), grid, block, 0, s, a, m);
   return hipGetLastError();
 }
 
@@ -76,28 +90,32 @@ hipError_t launch_decode(int io, const DecodeArgs &a, const DecodeMeta &m, hipSt
 // copy-per-draft verify: read once, then per token update, write a full copy,
 // and emit the output
 // ===========================================================================
-template <typename T>
+constexpr int kCopyR = 4;  // 16 KiB state tiles (see the decode tiles)
+
+template <typename T, int R>
 __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a, CopyMeta m) {
-  const Tile tl;
+  const TileR<R> tl;
   const Dims d = a.d;
+  constexpr int kTileRows = 8 * R;
+  const int pt_n = (d.P + kTileRows - 1) / kTileRows;
   int bid = blockIdx.x;
-  const int pt = bid % d.PT;
-  bid /= d.PT;
+  const int pt = bid % pt_n;
+  bid /= pt_n;
   const int h = bid % d.H;
   const int e = bid / d.H;
   const int slot = m.slot[e];
   const int src = m.src[e];
   const int g = h / (d.H / d.G);
-  const int prow0 = pt * kRows;
+  const int prow0 = pt * kTileRows;
   const bool colok = 4 * tl.c < d.N;
   const size_t PN = (size_t)d.P * d.N;
   const size_t tile_off = (size_t)prow0 * d.N + 4 * tl.c;
   const float *in = (src < 0 ? a.state + ((size_t)slot * d.H + h) * PN
                              : a.copies + (((size_t)slot * a.n_in_max + src) * d.H + h) * PN) +
                     tile_off;
-  float4 hv[8];
+  float4 hv[R];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < R; ++i) {
     const bool ok = colok && (prow0 + tl.row(i) < d.P);
     hv[i] = ok ? nt_load4(in + (size_t)tl.row(i) * d.N) : zero4();
   }
@@ -113,16 +131,16 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a, CopyMeta m) 
       Cv = Io<T>::ld4((const T *)a.C + (ek * d.G + g) * d.N + 4 * tl.c);
     }
     float *out = a.copies + (((size_t)slot * a.n_in_max + k) * d.H + h) * PN + tile_off;
-    float part[8];
+    float part[R];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
       const bool rowok = prow0 + tl.row(i) < d.P;
       const float u = rowok ? dt * Io<T>::ld(x + tl.row(i)) : 0.f;
       hv[i] = fma4(dA, hv[i], u, Bv);
       if (rowok && colok) nt_store4(out + (size_t)tl.row(i) * d.N, hv[i]);
       part[i] = dot4(hv[i], Cv);
     }
-    const float yv = reduce8(part, tl.lane);
+    const float yv = reduce_rows<R>(part, tl.lane);
     const int r = tl.reduced_row();
     if (tl.reduced_writer() && prow0 + r < d.P)
       Io<T>::st((T *)a.y + (ek * d.H + h) * d.P + prow0 + r, yv + Dh * Io<T>::ld(x + r));
@@ -130,11 +148,12 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a, CopyMeta m) 
 }
 
 hipError_t launch_copy(int io, const CopyArgs &a, const CopyMeta &m, hipStream_t s) {
-  dim3 grid(a.n * a.d.H * a.d.PT), block(kThreads);
+  const int pt_n = (a.d.P + 8 * kCopyR - 1) / (8 * kCopyR);
+  dim3 grid(a.n * a.d.H * pt_n), block(kThreads);
   if (io == kBF16)
-    hipLaunchKernelGGL(copy_kernel<bf16_t>, grid, block, 0, s, a, m);
+    hipLaunchKernelGGL((copy_kernel<bf16_t, kCopyR>), grid, block, 0, s, a, m);
   else
-    hipLaunchKernelGGL(copy_kernel<float>, grid, block, 0, s, a, m);
+    hipLaunchKernelGGL((copy_kernel<float, kCopyR>), grid, block, 0, s, a, m);
   return hipGetLastError();
 }
 
@@ -209,16 +228,21 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
 //   y_k = Lambda_m (ckpt . C_k) + sum_{j<=m} w_{j,m} x_j (B_j . C_k) + D x_k,
 // m = base + k, Lambda_m = exp(A sum_{i<=m} dt_i),
 // w_{j,m} = exp(A sum_{j<i<=m} dt_i) dt_j  (direct suffix sums, at most W terms).
-template <typename T>
+constexpr int kReplayR = 8;  // 32 KiB tiles: its per-workgroup setup (log staging, decay
+                             // weights) costs more than 16 KiB tiles gain
+
+template <typename T, int R>
 __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMeta m,
                                                           LogLayout lay) {
   extern __shared__ float smem[];
-  const Tile tl;
+  const TileR<R> tl;
+  constexpr int kRows = 8 * R;  // state rows of this workgroup's tile
   const Dims d = a.d;
   const int W = a.W, n_in = a.n_in;
+  const int pt_n = (d.P + kRows - 1) / kRows;
   int bid = blockIdx.x;
-  const int pt = bid % d.PT;
-  bid /= d.PT;
+  const int pt = bid % pt_n;
+  bid /= pt_n;
   const int h = bid % d.H;
   const int e = bid / d.H;
   const int slot = m.slot[e];
@@ -239,9 +263,9 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
 
   // checkpoint tile first
   float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * d.N + 4 * tl.c;
-  float4 hv[8];
+  float4 hv[R];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < R; ++i) {
     const bool ok = colok && (prow0 + tl.row(i) < d.P);
     hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * d.N) : zero4();
   }
@@ -329,17 +353,17 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   if (F > 0) {
     const float lam = s_flam[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < R; ++i)
       hv[i] = make_float4(lam * hv[i].x, lam * hv[i].y, lam * hv[i].z, lam * hv[i].w);
     for (int j = 0; j < F; ++j) {
       float4 Bv = zero4();
       if (colok) Bv = Io<T>::ld4(logB + (li.ent(slot, rh, j) * d.G + g) * d.N + 4 * tl.c);
       const float w = s_fw[j];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) hv[i] = fma4(1.f, hv[i], w * s_fx[j * kRows + tl.row(i)], Bv);
+      for (int i = 0; i < R; ++i) hv[i] = fma4(1.f, hv[i], w * s_fx[j * kRows + tl.row(i)], Bv);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < R; ++i)
       if (colok && prow0 + tl.row(i) < d.P) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
   }
 
@@ -347,10 +371,10 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   for (int k = 0; k < n_in; ++k) {
     float4 Cv = zero4();
     if (colok) Cv = Io<T>::ld4(inC + (((size_t)e * n_in + k) * d.G + g) * d.N + 4 * tl.c);
-    float part[8];
+    float part[R];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) part[i] = dot4(hv[i], Cv);
-    const float v = reduce8(part, tl.lane);
+    for (int i = 0; i < R; ++i) part[i] = dot4(hv[i], Cv);
+    const float v = reduce_rows<R>(part, tl.lane);
     if (tl.reduced_writer()) s_dot[k * kRows + tl.reduced_row()] = v;
   }
   __syncthreads();
@@ -368,6 +392,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
 }
 
 static size_t replay_smem_bytes(int W) {
+  constexpr int kRows = 8 * kReplayR;
   return sizeof(float) *
          ((size_t)W * kRows + W + W + W + (size_t)W * kRows + (size_t)W * kMaxInFlight +
           kMaxInFlight + (size_t)kMaxInFlight * kRows + 1);
@@ -384,12 +409,13 @@ hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  dim3 grid(a.n * a.d.H * a.d.PT), block(kThreads);
+  const int pt_n = (a.d.P + 8 * kReplayR - 1) / (8 * kReplayR);
+  dim3 grid(a.n * a.d.H * pt_n), block(kThreads);
   const size_t sm = replay_smem_bytes(a.W);
   if (io == kBF16)
-    hipLaunchKernelGGL(replay_kernel<bf16_t>, grid, block, sm, s, a, m, lay);
+    hipLaunchKernelGGL((replay_kernel<bf16_t, kReplayR>), grid, block, sm, s, a, m, lay);
   else
-    hipLaunchKernelGGL(replay_kernel<float>, grid, block, sm, s, a, m, lay);
+    hipLaunchKernelGGL((replay_kernel<float, kReplayR>), grid, block, sm, s, a, m, lay);
   return hipGetLastError();
 }
 
