@@ -74,13 +74,13 @@ struct TileR {
   __device__ __forceinline__ int row(int i) const { return 8 * i + 2 * wave + rsub; }
   // Row (within the tile) whose total this lane holds after reduce_rows<R>().
   __device__ __forceinline__ int reduced_row() const {
-    const int i = R == 8 ? ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1)
-                         : ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+    const int b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+    const int i = R == 8 ? b4 * 4 + b3 * 2 + b2 : R == 4 ? b4 * 2 + b3 : b4;
     return row(i);
   }
   // One lane of each group that holds the same reduced total.
   __device__ __forceinline__ bool reduced_writer() const {
-    return R == 8 ? (lane & 3) == 0 : (lane & 7) == 0;
+    return R == 8 ? (lane & 3) == 0 : R == 4 ? (lane & 7) == 0 : (lane & 15) == 0;
   }
 };
 typedef TileR<8> Tile;
@@ -125,13 +125,43 @@ __device__ __forceinline__ float reduce4(const float v[4], int lane) {
   s += __shfl_xor(s, 1);
   return s;
 }
+// Two-row variant.
+__device__ __forceinline__ float reduce2(const float v[2], int lane) {
+  float s = halve(v[0], v[1], (lane >> 4) & 1, 16);
+  s += __shfl_xor(s, 8);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  return s;
+}
 template <int R> __device__ __forceinline__ float reduce_rows(const float v[R], int lane);
+template <> __device__ __forceinline__ float reduce_rows<2>(const float v[2], int lane) {
+  return reduce2(v, lane);
+}
 template <> __device__ __forceinline__ float reduce_rows<8>(const float v[8], int lane) {
   return reduce8(v, lane);
 }
 template <> __device__ __forceinline__ float reduce_rows<4>(const float v[4], int lane) {
   return reduce4(v, lane);
 }
+
+// Sum over the 32 lanes of a row group with DPP lane moves (no LDS round
+// trip; the latency-critical form for the sequential scan).  Rotations by 1,
+// 2, 4 and 8 inside each 16-lane row leave every lane with its row's sum;
+// row_bcast:15 then adds row 0's sum into row 1 (and row 2's into row 3).
+// The 32-lane total is valid in lanes 16..31 and 48..63.
+#define SSM_DPP_ADD(v, ctrl)                                                                 \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), (ctrl), 0xF, 0xF, false))
+__device__ __forceinline__ float sum32_dpp(float v) {
+  SSM_DPP_ADD(v, 0x121);  // row_ror:1
+  SSM_DPP_ADD(v, 0x122);  // row_ror:2
+  SSM_DPP_ADD(v, 0x124);  // row_ror:4
+  SSM_DPP_ADD(v, 0x128);  // row_ror:8
+  // row_bcast:15 into rows 1 and 3 only (row_mask 0b1010)
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  return v;
+}
+#undef SSM_DPP_ADD
 
 // Streaming (nontemporal) 128-bit state accesses: the state is touched once
 // per step and the working set is far larger than the caches.
