@@ -32,6 +32,37 @@ HBM_PEAK_GBPS = 8000.0
 MIB = 1 << 20
 
 
+# HBM bytes of the decode kernel from two rocprofv3 --pmc passes (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch, mean of the 6 dispatches of
+# `bench.py --only decode --steps 5 --warmup 1`), each scaled by what the same
+# counter reads for a plain copy kernel of known size (ssm_state_init: 4 MiB
+# read + 4 MiB written per dispatch, `bench.py --only calib`).  Valid only for
+# the kernel sources they were taken on: a change to any of them turns the
+# figure into null until the counters are taken again.
+DECODE_COUNTERS = {
+    "sources": ["ssm_kernels.hip", "ssm_device.h", "ssm_internal.h"],
+    "sha256": "cfccd028b9f867ff6c937b67792f88e01115c9f92151808429270fdb0cff1f39",
+    "fetch_kib": 519388.11, "write_kib": 1056783.73,
+    "calib_fetch_kib": 2059.01, "calib_write_kib": 4096.0, "calib_true_kib": 4096.0,
+    "algorithmic_kib": 1035989.33 + 1056768.0,
+}
+
+
+def counter_traffic():
+    """Scaled HBM bytes per decode launch, or None if the kernel changed."""
+    import hashlib
+    c = DECODE_COUNTERS
+    h = hashlib.sha256()
+    for f in c["sources"]:
+        with open(os.path.join(ROOT, "streaming_state_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != c["sha256"]:
+        return None, None
+    kib = (c["fetch_kib"] * c["calib_true_kib"] / c["calib_fetch_kib"]
+           + c["write_kib"] * c["calib_true_kib"] / c["calib_write_kib"])
+    return round(kib * 1024), round(kib / c["algorithmic_kib"], 4)
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -83,7 +114,9 @@ def main():
     from streaming_state_amd import inputs
     from streaming_state_amd import ssm
     only = set(filter(None, args.only.split(",")))
-    want = (lambda k: not only or k in only)
+    want = (lambda k: (not only and k != "calib") or k in only)
+    if want("calib"):
+        return calib_copy(torch, ssm, args)
     K, Wm = args.steps, args.warmup
     dev = "cuda"
 
@@ -303,6 +336,7 @@ def main():
                            torch)
 
     dec_c = comp.get("decode", {})
+    traffic, traffic_ratio = counter_traffic()
     total_ms = sum(v["ms_mean"] for k, v in comp.items() if isinstance(v, dict) and "ms_mean" in v)
     line = {
         "metric": "decode state GB/s (% of HBM peak) at B=256; prefill tokens/s; replay vs copy speedup",
@@ -330,13 +364,36 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_c.get("GBps", 0.0), 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_c.get("GBps", 0.0) / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "decode_kernel<float>",
-                     "algorithmic_bytes_per_launch": dec_c.get("bytes_per_step")},
+                     "traffic": traffic, "kernel": "decode_kernel<float>",
+                     "algorithmic_bytes_per_launch": dec_c.get("bytes_per_step"),
+                     "traffic_over_algorithmic": traffic_ratio},
         "cpu_baseline": cpu,
         "extras": extras,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
+
+
+def calib_copy(torch, ssm, args):
+    """Counter calibration: the library's state copy (ssm_state_init) of 256
+    slots x 4 MiB = 1 GiB read + 1 GiB write, a plain copy kernel of known
+    size.  Prints the mean kernel time; counters are read by the profiler."""
+    H, P, N, S = 128, 64, 128, 256
+    A = torch.full((H,), -1.0, device="cuda")
+    D = torch.zeros(H, device="cuda")
+    h = ssm.StreamState(H, P, N, S, A, D)
+    src = torch.ones((S, H, P, N), device="cuda")
+    tm = Timer(torch)
+    for i in range(args.warmup + args.steps):
+        e = tm.start() if i >= args.warmup else None
+        h.init(list(range(S)), src)
+        if e is not None:
+            tm.stop(e)
+    torch.cuda.synchronize()
+    ms = float(np.mean(tm.ms()))
+    print(json.dumps({"calib": "copy_f32_kernel", "bytes_read": S * H * P * N * 4,
+                      "bytes_written": S * H * P * N * 4, "ms": ms,
+                      "GBps": 2 * S * H * P * N * 4 / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def cpu_baseline(inputs, dec_in, dec_reset, A, D, Bd, H, P, N, G, seconds, torch):
