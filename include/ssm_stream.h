@@ -198,7 +198,7 @@ ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
 size_t ssm_replay_log_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t W);
 
 /* Attach the caller's log buffer (device, ssm_replay_log_bytes bytes) with
- * window W (1 <= W <= 255).  Every slot's log starts empty; the slot's state
+ * window W (1 <= W <= 64).  Every slot's log starts empty; the slot's state
  * buffer is its checkpoint ("checkpoint: a full copy of the state, written
  * once per window", Glossary of the speculative-decoding page). */
 ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_bytes);
