@@ -8,11 +8,12 @@
  *     h_t = exp(dt_t[h] * A[h]) * h_{t-1} + dt_t[h] * x_t[h,:] (outer) B_t[g,:]
  *     y_t[h,p] = sum_n h_t[p,n] * C_t[g,n] + D[h] * x_t[h,p]
  *
- * ("decay the old state, then add the new token's contribution": "Why
- * Speculative Decoding Slows Hybrid Mamba Models at Large Batch Sizes",
- * section "The Fix: Log the Inputs, Checkpoint the State"; the matrix and
- * recurrent views of the same algebra: "Mamba Streaming State That Survives
- * Chunking", section "Separate Mamba-2 algebra from kernel behavior").
+ * (each token shrinks the previous state by its decay factor and adds its own
+ * outer-product term: "Why Speculative Decoding Slows Hybrid Mamba Models at
+ * Large Batch Sizes", section "The Fix: Log the Inputs, Checkpoint the State";
+ * the matrix and recurrent views of the same algebra: "Mamba Streaming State
+ * That Survives Chunking", section "Separate Mamba-2 algebra from kernel
+ * behavior").
  *
  * Three paths advance it, all on the caller's HIP stream:
  *   ssm_scan_chunk   a chunk of L tokens of one stream, with carry-in/out,
@@ -104,8 +105,9 @@ typedef struct {
                               w_i * (2*i + 1), modulo 2^64, i in [H,P,N] order */
 } ssm_receipt;
 
-/* Lifecycle counters ("Make reset, checkpoint, and cancellation observable":
- * keep metrics for resets, duplicate chunks, checkpoints, stale resumes).
+/* Lifecycle counters (resets, rejected duplicate or reordered chunks,
+ * checkpoints, rejected resumes: "Mamba Streaming State That Survives
+ * Chunking", section "Make reset, checkpoint, and cancellation observable").
  * Byte counters follow the algorithmic model (state bytes each path must
  * move), not hardware counters. */
 typedef struct {
@@ -135,9 +137,9 @@ ssm_status ssm_create(const ssm_layer_desc *desc, int32_t n_slots, float *d_stat
 ssm_status ssm_destroy(ssm_handle h);
 
 /* Reset h_slots[n] (distinct): state zeroed on `stream`, position 0, chunk_seq
- * 0, a new stream id, replay log emptied, any live copy dropped ("Reset
- * destroys the relationship with the prior stream": section "Make reset,
- * checkpoint, and cancellation observable"). */
+ * 0, a new stream id, replay log emptied, any live copy dropped: after a reset
+ * nothing of the earlier stream carries over (section "Make reset, checkpoint,
+ * and cancellation observable"). */
 ssm_status ssm_state_reset(ssm_handle h, int32_t n, const int32_t *h_slots, void *stream);
 
 /* Initialise h_slots[n] from a learned initial state d_init[n,H,P,N] (fp32,
@@ -156,8 +158,8 @@ size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc);
  *   chunk_seq   must equal the slot's next expected sequence number (0 after
  *               create/reset/init); a lower value is a duplicate, a higher one
  *               a reorder or gap: both return SSM_E_SEQUENCE with nothing
- *               changed ("Let the full scan define legal chunking": reordering
- *               or applying a chunk twice must fail).  On success the expected
+ *               changed (section "Let the full scan define legal chunking": a
+ *               chunk applied out of order or twice is an error).  On success the expected
  *               number becomes chunk_seq + 1; a retry of a chunk whose result
  *               was lost must restore a pre-chunk checkpoint first.
  *   L >= 0      L == 0 (an empty chunk) only advances chunk_seq.
@@ -180,8 +182,8 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
 
 /* ------------------------------------------------------------------ decode */
 
-/* One token for each of `batch` distinct slots h_slot_ids[batch] ("advances one
- * or a few positions across many streams": section "Separate Mamba-2 algebra
+/* One token for each of `batch` distinct slots h_slot_ids[batch] (decode moves
+ * many streams forward by a token each: section "Separate Mamba-2 algebra
  * from kernel behavior").  x[batch,H,P] dt[batch,H] B,C[batch,G,N] in, y[batch,H,P]
  * out (device, io dtype).  h_reset: host u8[batch] or NULL; a set flag starts
  * the slot from a zero state (its old state is not read) and position 0, so a
@@ -199,16 +201,17 @@ size_t ssm_replay_log_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t
 
 /* Attach the caller's log buffer (device, ssm_replay_log_bytes bytes) with
  * window W (1 <= W <= 64).  Every slot's log starts empty; the slot's state
- * buffer is its checkpoint ("checkpoint: a full copy of the state, written
- * once per window", Glossary of the speculative-decoding page). */
+ * buffer is its checkpoint (the Glossary of "Why Speculative Decoding Slows
+ * Hybrid Mamba Models at Large Batch Sizes": the checkpoint is a whole-state
+ * copy refreshed once per log window). */
 ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_bytes);
 
 /* Verify n_in (1 <= n_in <= W) in-flight tokens per slot (the real token plus
  * drafts).  For each slot, if the committed log length plus n_in exceeds W, the
  * log is first folded into the checkpoint (the only state write, fused into
  * this call).  Outputs of every in-flight token are computed from the
- * checkpoint and the log without writing the state ("The Fix: Log the Inputs,
- * Checkpoint the State"), and the in-flight inputs are appended to the log.
+ * checkpoint and the log without writing the state (section "The Fix: Log the
+ * Inputs, Checkpoint the State"), and the in-flight inputs are appended to the log.
  *   x[batch,n_in,H,P] dt[batch,n_in,H] B,C[batch,n_in,G,N]; y[batch,n_in,H,P]
  * Each slot must then be committed before its next replay step. */
 ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
@@ -229,8 +232,8 @@ size_t ssm_copy_buffer_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_
 /* Attach the caller's copy buffer d_copies[n_slots,n_in_max,H,P,N] (device). */
 ssm_status ssm_copy_attach(ssm_handle h, int32_t n_in_max, float *d_copies, size_t bytes);
 
-/* Baseline verify ("The Problem": save a full copy of the state after every
- * draft token): read each slot's live state once, and for each of the n_in
+/* Baseline verify (section "The Problem": the server keeps one full state copy
+ * per draft token so a rejected guess can be undone): read each slot's live state once, and for each of the n_in
  * tokens update it, write a full copy and emit the output.  Same layouts as
  * ssm_replay_step. */
 ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,

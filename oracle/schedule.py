@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 ReplaySSM keeps a checkpoint and a log of per-token inputs; the full state is
 written only when the log fills ("Why Speculative Decoding Slows Hybrid Mamba
 Models at Large Batch Sizes", section "The Fix: Log the Inputs, Checkpoint the
-State", and the Glossary entry "checkpoint": a full copy written once per
-window).  Reading used here: the log holds committed entries plus the n_in
+State", and the Glossary's checkpoint entry: a whole-state copy refreshed
+once per window).  Reading used here: the log holds committed entries plus the n_in
 in-flight entries of the current step, capacity W.  Before a step, if the
 committed length plus n_in would exceed W, the log is folded into the
 checkpoint (a flush) and the length restarts at 0; after the step the length

@@ -15,9 +15,9 @@
  *     s    <- a_t * s + dt_t[h] * x_t[h,:] (outer) B_t[g,:]
  *     y_t[h,p] = sum_n s[p,n] * C_t[g,n]  +  D[h] * x_t[h,p]
  *
- * This is the Mamba-2 selective-scan recurrence ("decay the old state, then
- * add the new token's contribution": "Why Speculative Decoding Slows Hybrid
- * Mamba Models at Large Batch Sizes", section "The Fix: Log the Inputs,
+ * This is the Mamba-2 selective-scan recurrence (each token scales the old
+ * state by its decay and adds its own term: "Why Speculative Decoding Slows
+ * Hybrid Mamba Models at Large Batch Sizes", section "The Fix: Log the Inputs,
  * Checkpoint the State"; the SSD dual view is named in "Mamba Streaming State
  * That Survives Chunking", section "Separate Mamba-2 algebra from kernel
  * behavior").  The output uses the post-update state.  A reset flag on token
@@ -27,8 +27,8 @@
  * Everything is fp64; inputs arrive already widened (exactly) from fp32 or
  * bf16.  Sums over n run in increasing n.  Compile with -ffp-contract=off so
  * the operation order is exactly the one written here, which makes a chunked
- * scan bit-identical to the full scan ("Let the full scan define legal
- * chunking": a scalar CPU fixture can demand exact values).
+ * scan bit-identical to the full scan (section "Let the full scan define
+ * legal chunking": a scalar CPU check may insist on exact equality).
  *
  * Threads only split independent (head) or (slot, head) units; each unit is a
  * strictly sequential loop over tokens, so results do not depend on the
@@ -203,8 +203,8 @@ static void dec_unit(void *vctx, int64_t u) {
 }
 
 /*
- * oracle_decode: one token per slot ("advances one or a few positions across
- * many streams": "Separate Mamba-2 algebra from kernel behavior").
+ * oracle_decode: one token per slot (decode moves many streams forward by a
+ * token each: section "Separate Mamba-2 algebra from kernel behavior").
  *   slot[batch] distinct slot indices into state[S,H,P,N] and pos[S]
  *   x[batch,H,P] dt[batch,H] B,C[batch,G,N]; reset[batch] or NULL
  *   y[batch,H,P]
@@ -300,9 +300,10 @@ int oracle_spec_step(int S, int H, int P, int N, int G, int batch, const int32_t
 /* ------------------------------------------------------------------------ */
 /*
  * oracle_replay_unrolled: outputs and folded state computed from a checkpoint
- * and a log of per-token inputs without stepping the state ("Today's output is
- * the checkpoint, decayed, plus each logged token's contribution, decayed by
- * how long ago it came": section "The Fix", paraphrased).  Used by the tests
+ * and a log of per-token inputs without stepping the state: the output is the
+ * decayed checkpoint's read-out plus every logged token's term, each decayed
+ * by the tokens that followed it (section "The Fix: Log the Inputs, Checkpoint
+ * the State").  Used by the tests
  * to pin the recurrence against the rearranged form; one head group, one slot.
  *
  * Entries 0..n_log-1 are the committed log, entries n_log..n_log+n_in-1 the

@@ -377,7 +377,8 @@ def test_spec_step_keeps_accepted_prefix():
 def test_replay_form_equals_recurrence(W):
     """Outputs from checkpoint + log (rearranged math) equal the step-by-step
     recurrence with rollback, within 1e-12, over random drafts and rejections
-    ("The Fix": the two differ by under a millionth of a millionth)."""
+    (section "The Fix: Log the Inputs, Checkpoint the State": the rearranged
+    form agrees with the recurrence to within 1e-12)."""
     H, P, N, n_in, steps = 2, 3, 4, 5, 14
     A, D = inputs.params(3, H)
     r = np.random.default_rng(W)
