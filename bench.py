@@ -291,8 +291,10 @@ def main():
         x1, dt1, B1, C1 = inputs.device_tokens(1, L1, H1, P, N, G, seed_extra=0)
         s1 = ssm.StreamState(H1, P, N, 1, torch.from_numpy(A1).to(dev),
                              torch.from_numpy(D1).to(dev), G=G)
+        y1 = torch.empty((L1, H1, P), dtype=torch.float32, device=dev)
         stream1 = {}
-        for chunk in (L1, 256, 64, 17, 1):
+        for chunk, wsm in ((L1, None), (256, None), (64, None), (17, None), (1, None),
+                           (L1, "serial"), (256, "serial"), (64, "serial")):
             s1.reset([0])
             sizes = [chunk] * (L1 // chunk) + ([L1 % chunk] if L1 % chunk else [])
             for rep in range(2):  # the first run warms caches
@@ -304,13 +306,14 @@ def main():
                 e0.record()
                 t = 0
                 for q, sz in enumerate(sizes):
-                    s1.scan_chunk(0, q, x1[t:t + sz], dt1[t:t + sz], B1[t:t + sz], C1[t:t + sz])
+                    s1.scan_chunk(0, q, x1[t:t + sz], dt1[t:t + sz], B1[t:t + sz], C1[t:t + sz],
+                                  y=y1[t:t + sz], workspace=wsm)
                     t += sz
                 e1.record()
                 torch.cuda.synchronize()
                 wall1 = time.perf_counter() - tw
             gpu_ms = e0.elapsed_time(e1)
-            stream1[str(chunk)] = dict(calls=len(sizes), tokens_per_s=L1 / (gpu_ms * 1e-3),
+            stream1[str(chunk) + ("_serial" if wsm else "")] = dict(calls=len(sizes), tokens_per_s=L1 / (gpu_ms * 1e-3),
                                        us_per_call=gpu_ms * 1e3 / len(sizes),
                                        host_wall_us_per_call=wall1 * 1e6 / len(sizes))
         extras["stream_130m"] = stream1

@@ -149,10 +149,19 @@ ssm_status ssm_state_init(ssm_handle h, int32_t n, const int32_t *h_slots, const
 
 /* ----------------------------------------------------------- chunked scan */
 
-/* Bytes of device workspace ssm_scan_chunk may need (H*P*N*4).  It is used
- * only when a chunk both carries state in (no reset on its first token) and
- * holds a reset later; otherwise d_workspace may be NULL. */
-size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc);
+/* Bytes of device workspace for ssm_scan_chunk on chunks of up to L tokens
+ * (0 for an invalid desc or L < 0).  Two forms of the scan exist, with the same
+ * results up to floating-point rounding order:
+ *   - tile-parallel (fp32 io, or bf16 shapes other than P=64/N=128; P of 32 or
+ *     64 and N a multiple of 32): chunks of 64 tokens or more run in parallel
+ *     over 64-token tiles.  It needs this many bytes (per-tile states, at most
+ *     64 tiles at a time: min(ceil(L/64), 64)*H*P*N*4 + 256*H bytes) and x
+ *     aligned to 4 elements;
+ *   - recurrent / SSD: needs H*P*N*4 bytes only when a chunk both carries state
+ *     in (no reset on its first token) and holds a reset later; otherwise
+ *     d_workspace may be NULL.
+ * A workspace smaller than the tile-parallel form's need selects the other. */
+size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc, int64_t L);
 
 /* Advance stream `slot` by the L tokens of one chunk.
  *   chunk_seq   must equal the slot's next expected sequence number (0 after

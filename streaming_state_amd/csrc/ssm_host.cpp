@@ -133,6 +133,14 @@ ssm_status check_desc(const ssm_layer_desc *desc) {
   return SSM_OK;
 }
 
+Dims dims_of(const ssm_layer_desc *desc) {
+  return Dims{desc->H, desc->P, desc->N, desc->G, (desc->P + kRows - 1) / kRows};
+}
+
+// Shortest chunk that takes the tile-parallel form: below it the three passes
+// cost more than walking the tokens.
+constexpr int64_t kChunkMinTokens = 64;
+
 // Validate a batch of slot ids: in range and pairwise distinct.
 ssm_status check_slots(Handle *H, int n, const int32_t *slots, const char *what) {
   if (n < 0) return fail(SSM_E_INVALID_ARG, "%s: negative count", what);
@@ -287,7 +295,7 @@ ssm_status ssm_create(const ssm_layer_desc *desc, int32_t n_slots, float *d_stat
   if (!aligned(d_state, 16)) return fail(SSM_E_INVALID_ARG, "state must be 16-byte aligned");
   Handle *H = new Handle();
   H->desc = *desc;
-  H->d = Dims{desc->H, desc->P, desc->N, desc->G, (desc->P + kRows - 1) / kRows};
+  H->d = dims_of(desc);
   H->io = desc->io_dtype;
   H->S = n_slots;
   H->state = d_state;
@@ -357,9 +365,14 @@ ssm_status ssm_state_init(ssm_handle h, int32_t n, const int32_t *h_slots, const
 }
 
 // ------------------------------------------------------------------- scan
-size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc) {
-  if (!desc || desc->H < 1 || desc->P < 1 || desc->N < 1) return 0;
-  return (size_t)desc->H * desc->P * desc->N * sizeof(float);
+size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc, int64_t L) {
+  if (check_desc(desc) != SSM_OK || L < 0) return 0;
+  const Dims d = dims_of(desc);
+  const size_t state = (size_t)d.H * d.P * d.N * sizeof(float);
+  if (ssd_supported(desc->io_dtype, d) || !chunk_supported(desc->io_dtype, d) ||
+      L < kChunkMinTokens)
+    return state;
+  return std::max(state, chunk_ws_floats(d, L) * sizeof(float));
 }
 
 ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_t L,
@@ -403,6 +416,49 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
     return fail(SSM_E_INVALID_ARG, "scan: bf16 x, B and C must be 16-byte aligned");
   if ((n_ckpt > 0 && !aligned(d_ckpt_out, 16)) || !aligned(d_workspace, 16))
     return fail(SSM_E_INVALID_ARG, "scan: checkpoint and workspace buffers must be 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  // Tile-parallel form: long enough chunks of the shapes it covers, given the
+  // workspace it needs; otherwise the recurrent form (same results up to
+  // rounding order).
+  const bool par = !ssd && chunk_supported(H->io, H->d) && L >= kChunkMinTokens &&
+                   aligned(x, 4 * io_size(H->io)) && d_workspace &&
+                   ws_bytes >= chunk_ws_floats(H->d, L) * sizeof(float);
+  if (par) {
+    st = check_finite(H, s, {{x, (size_t)L * H->d.H * H->d.P}, {dt, (size_t)L * H->d.H},
+                             {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
+    if (st != SSM_OK) return st;
+    const int64_t piece = (int64_t)kChunkTile * kChunkTilesPerLaunch;
+    for (int64_t t0 = 0; t0 < L; t0 += piece) {
+      const int len = (int)std::min<int64_t>(piece, L - t0);
+      ChunkArgs a{};
+      ChunkMeta m{};
+      a.x = x;
+      a.dt = dt;
+      a.B = B;
+      a.C = C;
+      a.y = y;
+      a.state = H->slot_state(slot);
+      a.ws = (float *)d_workspace;
+      a.lam = a.ws + chunk_ws_floats(H->d, L) - (size_t)kChunkTilesPerLaunch * H->d.H;
+      a.ckpt_out = d_ckpt_out;
+      a.A = H->A;
+      a.D = H->D;
+      a.d = H->d;
+      a.t0 = (int)t0;
+      a.len = len;
+      a.n_tiles = (len + kChunkTile - 1) / kChunkTile;
+      if (h_reset)
+        for (int j = 0; j < len; ++j)
+          if (h_reset[t0 + j]) m.rmask[j / kChunkTile] |= 1ull << (j % kChunkTile);
+      for (int i = 0; i < n_ckpt; ++i)
+        if (h_ckpt_at[i] >= t0 && h_ckpt_at[i] < t0 + len) {
+          m.ck_t[a.n_ck] = (int32_t)h_ckpt_at[i];
+          m.ck_idx[a.n_ck] = i;
+          ++a.n_ck;
+        }
+      HIP_TRY(launch_chunk(H->io, a, m, s));
+    }
+  }
   // segments: runs between resets
   std::vector<ScanSeg> segs;
   {
@@ -415,20 +471,19 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
       }
     }
   }
-  const bool need_ws = segs.size() > 1 && segs.front().init;
+  const bool need_ws = !par && segs.size() > 1 && segs.front().init;
   segs.back().final = need_ws ? 2 : 1;
   if (need_ws && (!d_workspace || ws_bytes < H->state_bytes()))
     return fail(SSM_E_INVALID_ARG,
                 "scan: this chunk carries state in and resets later; it needs a workspace of "
                 "%zu bytes",
                 H->state_bytes());
-  hipStream_t s = as_stream(stream);
-  const size_t es = io_size(H->io);
-  st = check_finite(H, s, {{x, (size_t)L * H->d.H * H->d.P}, {dt, (size_t)L * H->d.H},
-                           {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
-  if (st != SSM_OK) return st;
-  (void)es;
-  for (size_t i0 = 0; i0 < segs.size(); i0 += kSegPerLaunch) {
+  if (!par) {
+    st = check_finite(H, s, {{x, (size_t)L * H->d.H * H->d.P}, {dt, (size_t)L * H->d.H},
+                             {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
+    if (st != SSM_OK) return st;
+  }
+  for (size_t i0 = 0; !par && i0 < segs.size(); i0 += kSegPerLaunch) {
     const int ns = (int)std::min<size_t>(kSegPerLaunch, segs.size() - i0);
     ScanMeta m{};
     for (int i = 0; i < ns; ++i) m.seg[i] = segs[i0 + i];

@@ -116,6 +116,35 @@ hipError_t launch_scan(int io, const ScanArgs &a, const ScanMeta &m, hipStream_t
 bool ssd_supported(int io, const Dims &d);
 hipError_t launch_scan_ssd(const ScanArgs &a, const ScanMeta &m, hipStream_t s);
 
+// -------------------------------------------------- scan, tile-parallel form
+// Tiles of kChunkTile tokens; at most kChunkTilesPerLaunch tiles per launch
+// (longer chunks run as consecutive pieces, each carrying the state through
+// the slot buffer).
+constexpr int kChunkTile = 64;
+constexpr int kChunkTilesPerLaunch = 64;
+struct ChunkMeta {
+  uint64_t rmask[kChunkTilesPerLaunch];  // bit j: reset before token j of the tile
+  int32_t ck_t[kCkptPerLaunch];          // chunk token index (post-token state)
+  int32_t ck_idx[kCkptPerLaunch];        // destination index into ckpt_out
+};
+struct ChunkArgs {
+  const void *x, *dt, *B, *C;  // the whole chunk (token 0 of the chunk)
+  void *y;
+  float *state;     // the slot's [H, P, N]: carry-in, then carry-out
+  float *ws;        // [n_tiles][H][P][N]: tile states, then tile carry-ins
+  float *lam;       // [n_tiles][H]: tile decays (0: a reset inside the tile)
+  float *ckpt_out;  // [n_ckpt, H, P, N]
+  const float *A, *D;
+  Dims d;
+  int t0, len;      // this piece: tokens [t0, t0 + len) of the chunk
+  int n_tiles, n_ck;
+};
+// Shapes the tile-parallel form covers (P in {32, 64}, N a multiple of 32 up
+// to 128); workspace floats it needs for a chunk of L tokens.
+bool chunk_supported(int io, const Dims &d);
+size_t chunk_ws_floats(const Dims &d, int64_t L);
+hipError_t launch_chunk(int io, const ChunkArgs &a, const ChunkMeta &m, hipStream_t s);
+
 // --------------------------------------------------------------- state ops
 hipError_t launch_zero(float *dst, size_t n_floats, hipStream_t s);
 hipError_t launch_copy_f32(float *dst, const float *src, size_t n_floats, hipStream_t s);

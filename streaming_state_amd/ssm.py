@@ -101,7 +101,7 @@ _SIGS = {
     "ssm_destroy": [_H],
     "ssm_state_reset": [_H, _I32, _V, _V],
     "ssm_state_init": [_H, _I32, _V, _V, _V],
-    "ssm_scan_workspace_bytes": [ctypes.POINTER(LayerDesc)],
+    "ssm_scan_workspace_bytes": [ctypes.POINTER(LayerDesc), _I64],
     "ssm_scan_chunk": [_H, _I32, _U64, _I64, _V, _V, _V, _V, _V, _V, _I32, _V, _V, _V, _SZ, _V],
     "ssm_decode_step": [_H, _I32, _V, _V, _V, _V, _V, _V, _V, _V],
     "ssm_replay_log_bytes": [ctypes.POINTER(LayerDesc), _I32, _I32],
@@ -218,6 +218,7 @@ class StreamState:
         self.log = None
         self.copies = None
         self.workspace = None
+        self._ws_serial = None
 
     # -------------------------------------------------------------- lifecycle
     def destroy(self):
@@ -236,8 +237,29 @@ class StreamState:
                                    _stream(stream)))
 
     # ------------------------------------------------------------------ scan
+    def scan_workspace_bytes(self, L):
+        return int(_lib.ssm_scan_workspace_bytes(ctypes.byref(self.desc), int(L)))
+
+    def _scan_workspace(self, L, workspace, device):
+        """None: a cached buffer sized for L (the fastest form); "serial": one
+        state's worth (the recurrent form); a tensor: used as given."""
+        torch = _torch()
+        if workspace is not None and not isinstance(workspace, str):
+            return workspace
+        if workspace == "serial":
+            nb = self.H * self.P * self.N * 4
+            if self._ws_serial is None:
+                self._ws_serial = torch.empty(nb, dtype=torch.uint8, device=device)
+            return self._ws_serial
+        if workspace is not None:
+            raise ValueError(f"unknown workspace mode {workspace!r}")
+        nb = self.scan_workspace_bytes(L)
+        if self.workspace is None or self.workspace.numel() < nb:
+            self.workspace = torch.empty(nb, dtype=torch.uint8, device=device)
+        return self.workspace
+
     def scan_chunk(self, slot, chunk_seq, x, dt, B, C, y=None, reset=None, ckpt_at=None,
-                   ckpt_out=None, stream=None):
+                   ckpt_out=None, stream=None, workspace=None):
         torch = _torch()
         L = x.shape[0]
         H, P, N, G = self.H, self.P, self.N, self.G
@@ -250,13 +272,7 @@ class StreamState:
         n_ck = len(ck)
         if n_ck and ckpt_out is None:
             ckpt_out = torch.empty((n_ck, H, P, N), dtype=torch.float32, device=x.device)
-        need_ws = rs is not None and L > 0 and not rs[0] and rs[1:].any()
-        ws = None
-        if need_ws:
-            if self.workspace is None:
-                nb = _lib.ssm_scan_workspace_bytes(ctypes.byref(self.desc))
-                self.workspace = torch.empty(nb, dtype=torch.uint8, device=x.device)
-            ws = self.workspace
+        ws = self._scan_workspace(L, workspace, x.device)
         dt_ = self.io_dtype
         _check(_lib.ssm_scan_chunk(
             self.handle, int(slot), int(chunk_seq), int(L),

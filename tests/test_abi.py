@@ -158,7 +158,17 @@ def test_restore_rejects_incompatible_receipts():
 def test_size_queries():
     lib = ssm.lib()
     d = _desc(H=128, P=64, N=128)
-    assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 128 * 64 * 128 * 4
+    state = 128 * 64 * 128 * 4
+    # fp32 io at P=64, N=128: the tile-parallel form needs one state per
+    # 64-token tile (at most 64 tiles at a time) plus 64 decays per head
+    ws = lib.ssm_scan_workspace_bytes
+    assert ws(ctypes.byref(d), 1) == state
+    assert ws(ctypes.byref(d), 2048) == 32 * state + 64 * 128 * 4
+    assert ws(ctypes.byref(d), 65536) == 64 * state + 64 * 128 * 4
+    assert ws(ctypes.byref(d), -1) == 0
+    # bf16 at P=64, N=128 takes the SSD form; P=4 only the recurrent form
+    assert ws(ctypes.byref(_desc(H=128, P=64, N=128, io=ssm.SSM_BF16)), 65536) == state
+    assert ws(ctypes.byref(_desc(H=2, P=4, N=8)), 4096) == 2 * 4 * 8 * 4
     assert lib.ssm_copy_buffer_bytes(ctypes.byref(d), 256, 5) == 256 * 5 * 4 * 1024 * 1024
     # the log holds two halves of W entries of dt[H], x[H,P], B[G,N] per slot
     entry = (128 + 128 * 64 + 128) * 4

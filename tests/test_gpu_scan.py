@@ -22,13 +22,13 @@ def ssm():
     return m
 
 
-def _stream_chunks(h, slot, sizes, dev, reset=None):
+def _stream_chunks(h, slot, sizes, dev, reset=None, workspace=None):
     """Scan dev tensors chunk by chunk; return concatenated y."""
     ys, t0 = [], 0
     for seq, s in enumerate(sizes):
         sl = slice(t0, t0 + s)
         y = h.scan_chunk(slot, seq, dev[0][sl], dev[1][sl], dev[2][sl], dev[3][sl],
-                         reset=None if reset is None else reset[sl])
+                         reset=None if reset is None else reset[sl], workspace=workspace)
         ys.append(y)
         t0 += s
     return torch.cat(ys) if ys else None
@@ -75,19 +75,22 @@ def test_workload0_reset_separation(ssm):
     assert h.position(0)[0] == L - k
 
 
-@pytest.mark.parametrize("chunk", [None, 256, 64, 17, 1])
-def test_workload1_streaming(ssm, chunk):
+@pytest.mark.parametrize("chunk,ws", [(None, None), (None, "serial"), (256, None), (64, None),
+                                      (17, None), (1, None)])
+def test_workload1_streaming(ssm, chunk, ws):
     """Mamba-130M-shaped layer (H=24, P=64, N=128, L=2048, fp32): full scan and
-    chunked streaming with the state carried across chunks."""
+    chunked streaming with the state carried across chunks.  Chunks of 64
+    tokens or more take the tile-parallel form; ws="serial" forces the
+    recurrent form on the full scan."""
     w = inputs.workload1()
     L, H, P, N = w["L"], w["H"], w["P"], w["N"]
-    say("workload1 chunk", chunk)
+    say("workload1 chunk", chunk, ws)
     ref = oracle.scan(w["x"], w["dt"], w["B"], w["C"], w["A"], w["D"], n_threads=None)
     dev = [to_dev(w[k]) for k in ("x", "dt", "B", "C")]
     h = ssm.StreamState(H, P, N, 1, to_dev(w["A"]), to_dev(w["D"]))
     h.reset([0])
     sizes = [L] if chunk is None else [chunk] * (L // chunk) + ([L % chunk] if L % chunk else [])
-    y = _stream_chunks(h, 0, sizes, dev)
+    y = _stream_chunks(h, 0, sizes, dev, workspace=ws)
     torch.cuda.synchronize()
     assert_close(host(y), ref["y"], what="y", **F32_TOL)
     assert_close(host(h.state[0]), ref["state"], what="state", **F32_TOL)
@@ -126,6 +129,54 @@ def test_ragged_resets_checkpoints(ssm, H, P, N, G, io, L):
     assert_close(host(h.state[1]), ref["state"], what="carry-out", **tol(ref["state"]))
     # the last reset fixes the position: tokens after it
     assert h.position(1) == (ref["pos"], 1) and ref["pos"] == L - (2 * L) // 3
+
+
+@pytest.mark.parametrize("H,P,N,G,io,L,resets,ck", [
+    # resets inside tiles (one doubled, one on a checkpoint token), checkpoints
+    # on tile edges and on the last token
+    (3, 64, 128, 1, "f32", 300, [70, 100, 101, 190], [5, 63, 64, 100, 150, 299]),
+    # more than 64 tiles: two launches, the carry passing through the slot
+    (4, 32, 64, 2, "f32", 4200, [1000, 4096, 4100], [4095, 4096, 4199]),
+    # bf16 io outside the SSD form's shape
+    (2, 32, 96, 1, "bf16", 257, [128], [0, 127, 256]),
+    # one full tile that starts with a reset: the carried-in state is dropped
+    (2, 64, 128, 1, "f32", 64, [0, 40], [63]),
+    # a reset on a tile's first token, ragged last tile
+    (5, 64, 32, 5, "f32", 200, [64, 128], [199]),
+])
+def test_tile_parallel_form(ssm, H, P, N, G, io, L, resets, ck):
+    """The tile-parallel scan (fp32 MFMA) against the oracle: carry-in from a
+    learned state, per-token resets inside and on tile edges, checkpoints."""
+    say("scan tile-parallel", H, P, N, G, io, L)
+    r = np.random.default_rng(L + P)
+    x, dt, B, C = inputs.tokens(31, L, H, P, N, G)
+    A, D = inputs.params(31, H)
+    if io == "bf16":
+        bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
+        x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
+        dev = [bf16_dev(a) for a in bits]
+    else:
+        dev = [to_dev(a) for a in (x, dt, B, C)]
+    st0 = r.standard_normal((H, P, N)).astype(np.float32) * 0.05
+    reset = np.zeros(L, np.uint8)
+    reset[resets] = 1
+    ref = oracle.scan(x, dt, B, C, A, D, state=st0, pos=5, reset=reset, ckpt_at=ck,
+                      n_threads=None)
+    h = ssm.StreamState(H, P, N, 2, to_dev(A), to_dev(D), G=G, io_dtype=io)
+    h.init([1], to_dev(st0[None]))
+    assert h.scan_workspace_bytes(L) > H * P * N * 4
+    y, cko = h.scan_chunk(1, 0, *dev, reset=reset, ckpt_at=ck)
+    torch.cuda.synchronize()
+    tol = (lambda a: bf16_tol(a)) if io == "bf16" else (lambda a: F32_TOL)
+    assert_close(host(y), ref["y"], what="y", **tol(ref["y"]))
+    assert_close(host(cko), ref["ckpt"], what="checkpoints", **tol(ref["ckpt"]))
+    assert_close(host(h.state[1]), ref["state"], what="carry-out", **tol(ref["state"]))
+    assert h.position(1) == (ref["pos"], 1)
+    # deterministic: the same chunk again from the same state gives the same bits
+    h.init([0], to_dev(st0[None]))
+    y2, cko2 = h.scan_chunk(0, 0, *dev, reset=reset, ckpt_at=ck)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(cko, cko2) and torch.equal(h.state[0], h.state[1])
 
 
 def test_empty_chunk_is_neutral(ssm):
