@@ -10,18 +10,26 @@
 //   h_new[p,n]  = exp(cs_end) h_prev[p,n]
 //               + sum_s exp(cs_end - cs_s) dt_s x[s,p] B[s,n]            (G3)
 //   y = Y_diag + Y_off + D x
-// One workgroup (4 waves) owns one (segment, head): a segment is a run of
+// One workgroup (8 waves) owns one (segment, head): a segment is a run of
 // tokens between resets, so it starts from the carried-in state or from zero
-// and no reset falls inside it.  The fp32 state h^T[n,p] stays in MFMA
-// accumulators across blocks (wave w owns n in [32w, 32w+32)); a bf16 copy in
-// LDS feeds G4 of the next block.  Blocks end early at checkpoint tokens so the
+// and no reset falls inside it.  Roles, in the two compute phases of a block:
+//   waves 0-3  own the four 32 x 32 tiles of y: G4, then G2 and the epilogue;
+//   waves 4-7  own the fp32 state h^T[n,p] in MFMA accumulators for the whole
+//              segment (wave 4+i: n in [32i, +32), both p tiles); waves 4-6
+//              first compute the three tiles of C.B on or below the diagonal
+//              (G1) and mask them into M, then all four run G3 (beside G2),
+//              the checkpoints and the bf16 copy of h that feeds G4.
+// All eight stage the next block's inputs.  Two workgroups share a CU, so each
+// SIMD holds four waves.  Blocks end early at checkpoint tokens so the
 // post-token state can be written from the accumulators.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Operand lane layout (A: 32 x 16, B: 16 x 32):
 // lane l supplies row/column l%32 and K indices 8*(l/32) .. +7; accumulator
-// register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Every
-// operand is read from LDS as one 16-byte row segment, so each operand tile is
-// staged in the orientation that puts K contiguous.
+// register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+// Operands whose K runs along an LDS row are read as 16-byte segments; those
+// whose K runs down the rows of a row-major tile (B^T for G3, x for G2 and
+// G3) are read with the LDS transposing load ds_read_b64_tr_b16, so every
+// input is staged once, row-major, straight from coalesced global loads.
 #include "ssm_device.h"
 
 namespace ssm {
@@ -29,33 +37,47 @@ namespace ssm {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+constexpr int kSsdThreads = 512;  // 8 waves
 constexpr int Q = 64;    // tokens per block
 constexpr int SP = 64;   // head dim
 constexpr int SN = 128;  // state size
 
-// Rows of 128 bf16 (C, B, h) are unpadded with their 16-byte chunks
-// XOR-swizzled by row; rows of 64 bf16 (the transposed tiles) are padded to 72
-// so that the scattered 2-byte transposing writes have linear addresses.
-// Either way the 32 rows one MFMA operand read touches fall on distinct banks.
-constexpr int LDT = Q + 8;
-__device__ __forceinline__ int sw128(int row, int col) {
-  return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
+// LDS layouts.  Rows are unpadded; 16-byte chunks are XOR-swizzled by row so
+// that both access patterns of a tile are free of bank conflicts on the
+// 64-bank LDS:
+//  - 256-byte rows (C, B, h: 128 bf16): chunk ^ f(row), f(r) = (r%4)*4 + (r/4)%4.
+//    A 16-row read of one chunk hits 16 distinct chunks (f is a bijection of
+//    0..15); a transposing read covers rows r..r+3 (r % 4 == 0) x 4 chunks of
+//    an aligned quad, and f moves each row's quad to a different quad.
+//  - 128-byte rows (x, w*x: 64 bf16) are only read transposed: chunk ^ 4 on
+//    rows with bit 1 set separates rows r and r+2, which share banks.
+//  - 128-byte rows of M^T (read as 16-row segments): chunk ^ ((row / 2) % 8).
+__device__ __forceinline__ int sw_n(int row, int col) {  // element index, 128-wide rows
+  const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+  return row * SN + ((((col >> 3) ^ f)) << 3) + (col & 7);
+}
+__device__ __forceinline__ int sw_x(int row, int col) {  // 64-wide rows, transposed reads
+  return row * SP + ((((col >> 3) ^ ((row & 2) << 1))) << 3) + (col & 7);
+}
+__device__ __forceinline__ int sw_m(int row, int col) {  // 64-wide rows, row reads
+  return row * Q + ((((col >> 3) ^ ((row >> 1) & 7))) << 3) + (col & 7);
 }
 
-// 78 KiB: two workgroups fit in one CU's 160 KiB.
+// 72 KiB: two workgroups per CU.
 struct Smem {
-  bf16_t C[Q * SN];          // C[t][n]                     (swizzled)
-  bf16_t R[2 * Q * LDT];     // B[s][n] (swizzled) until G1 is done, then
-                             // M^T[t][s] and (w x)^T[p][s] (padded)
-  bf16_t BT[SN * LDT];       // B[s][n] stored [n][s]       (padded)
-  bf16_t Xt[SP * LDT];       // x[s][p] stored [p][s]       (padded)
-  bf16_t HT[SP * SN];        // bf16 copy of h_prev[p][n]   (swizzled)
-  float dt[Q], cs[Q], ecs[Q], w[Q];
+  bf16_t C[Q * SN];   // C[t][n]
+  bf16_t B[Q * SN];   // B[s][n]
+  bf16_t HT[SP * SN]; // bf16 copy of h_prev[p][n]
+  bf16_t X[Q * SP];   // x[s][p]
+  bf16_t XW[Q * SP];  // w_s x[s][p]
+  bf16_t MT[Q * Q];   // M[t][s] (masked C.B with D on the diagonal)
+  float cs[Q], ecs[Q], dt[Q];
   float lam;
 };
-static_assert(2 * Q * LDT >= Q * SN, "R must hold B row-major");
 static_assert(2 * sizeof(Smem) <= 160 * 1024, "two workgroups per CU");
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -64,6 +86,31 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 __device__ __forceinline__ bf16x8_t lds8(const bf16_t *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
 }
+__device__ __forceinline__ s16x4_t ldtr4(const bf16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t *)(p));
+}
+// An MFMA operand whose 8 K values run down rows k0..k0+7 of a row-major tile,
+// at column col0 + l%16 of the lane's 16-lane group (col0 is the group's first
+// column): two transposing reads of 4 rows each.  Lane l of a 16-lane group
+// supplies row k0 + 4r + (l%16)/4, columns col0 + 4(l%4) .. +3; the hardware
+// hands lane j element j%4 of the segments of lanes j/4, 4 + j/4, 8 + j/4 and
+// 12 + j/4, i.e. column col0 + j of rows k0 + 4r .. +3.
+template <typename SW>
+__device__ __forceinline__ bf16x8_t ldtr8(const bf16_t *tile, int k0, int col0, int lane, SW sw) {
+  const int rr = (lane & 15) >> 2, cc = col0 + 4 * (lane & 3);
+  const s16x4_t lo = ldtr4(tile + sw(k0 + rr, cc));
+  const s16x4_t hi = ldtr4(tile + sw(k0 + 4 + rr, cc));
+  const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+struct SwN {
+  __device__ __forceinline__ int operator()(int r, int c) const { return sw_n(r, c); }
+};
+struct SwX {
+  __device__ __forceinline__ int operator()(int r, int c) const { return sw_x(r, c); }
+};
+
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll
@@ -80,16 +127,16 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return v;
 }
 
-// h^T accumulators (two 32 x 32 tiles: n in [32w, 32w+32), p-tile j) <-> a
-// [P][N] fp32 state tile.  Register r of lane l is h[p = 32j + l%32][n = 32w +
+// h^T accumulator tiles (n in [32 nt, +32), p tile j = 0, 1) <-> a [P][N] fp32
+// state.  Register r of lane l of tile j is h[p = 32j + l%32][n = 32nt +
 // acc_row(r)], so four consecutive registers are four consecutive n.
-__device__ __forceinline__ void state_load(f32x16_t hacc[2], const float *src, int wave, int l32,
+__device__ __forceinline__ void state_load(f32x16_t hacc[2], const float *src, int nt, int l32,
                                            int hi) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int p = 32 * j + l32, n = 32 * wave + 8 * q + 4 * hi;
+      const int p = 32 * j + l32, n = 32 * nt + 8 * q + 4 * hi;
       const float4 v = *reinterpret_cast<const float4 *>(src + (size_t)p * SN + n);
       hacc[j][4 * q + 0] = v.x;
       hacc[j][4 * q + 1] = v.y;
@@ -97,104 +144,118 @@ __device__ __forceinline__ void state_load(f32x16_t hacc[2], const float *src, i
       hacc[j][4 * q + 3] = v.w;
     }
 }
-__device__ __forceinline__ void state_store(const f32x16_t hacc[2], float *dst, int wave, int l32,
+__device__ __forceinline__ void state_store(const f32x16_t hacc[2], float *dst, int nt, int l32,
                                             int hi) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int p = 32 * j + l32, n = 32 * wave + 8 * q + 4 * hi;
+      const int p = 32 * j + l32, n = 32 * nt + 8 * q + 4 * hi;
       *reinterpret_cast<float4 *>(dst + (size_t)p * SN + n) =
           make_float4(hacc[j][4 * q], hacc[j][4 * q + 1], hacc[j][4 * q + 2], hacc[j][4 * q + 3]);
     }
 }
-__device__ __forceinline__ void state_to_lds(const f32x16_t hacc[2], bf16_t *HT, int wave, int l32,
+__device__ __forceinline__ void state_to_lds(const f32x16_t hacc[2], bf16_t *HT, int nt, int l32,
                                              int hi) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int p = 32 * j + l32, n = 32 * wave + 8 * q + 4 * hi;
-      *reinterpret_cast<uint2 *>(HT + sw128(p, n)) =
+      const int p = 32 * j + l32, n = 32 * nt + 8 * q + 4 * hi;
+      *reinterpret_cast<uint2 *>(HT + sw_n(p, n)) =
           pack4(hacc[j][4 * q], hacc[j][4 * q + 1], hacc[j][4 * q + 2], hacc[j][4 * q + 3]);
     }
 }
 
 // One block's global inputs, held in registers between the load and the LDS
-// write so the loads overlap the previous block's compute.
+// write so the loads overlap the previous block's compute.  Thread q takes
+// 16-byte chunks q and q + 512 of the C and B tiles (16 chunks per row) and
+// chunk q of the x tile (8 per row): every wave reads whole rows, so the loads
+// are coalesced.  Every lane of every wave also reads the dt of token `lane`
+// (the running sums are computed in each wave).  Loads are unconditional (rows
+// past the block end re-read its last row) so nothing waits until the values
+// are written to LDS; stage_store zeroes those rows.
 struct Staged {
-  uint4 c[4], b[4], x[2];
+  uint4 c[2], b[2], x;
   uint32_t dt;  // raw bf16 bits
 };
 
-// Thread layout of the staging: in pass k, wave w handles 16-byte chunk
-// c = w + 4k of every token row, one row per lane (row = lane).  Each
-// transposing write then covers 64 consecutive tokens of one row of B^T / x^T,
-// and lane pairs (2i, 2i+1) swap halves so that each lane writes 4-byte words
-// holding two consecutive tokens: bank-conflict-free.  Loads are
-// unconditional (rows past the block end re-read its last row) so no wait is
-// needed until the values are written to LDS; stage_store zeroes those rows.
 __device__ __forceinline__ void stage_load(Staged &st, const ScanArgs &a, int t0, int len, int h,
-                                           int g, int lane, int wave) {
+                                           int g, int tid, int lane) {
   const Dims &d = a.d;
   const bf16_t *Cg = (const bf16_t *)a.C, *Bg = (const bf16_t *)a.B;
   const bf16_t *xg = (const bf16_t *)a.x, *dtg = (const bf16_t *)a.dt;
-  const int row = t0 + min(lane, len - 1);
-  const size_t rowCB = ((size_t)row * d.G + g) * SN;
-  const size_t rowX = ((size_t)row * d.H + h) * SP;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c8 = (wave + 4 * k) * 8;
-    st.c[k] = *reinterpret_cast<const uint4 *>(Cg + rowCB + c8);
-    st.b[k] = *reinterpret_cast<const uint4 *>(Bg + rowCB + c8);
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + kSsdThreads * k;
+    const int row = t0 + min(q >> 4, len - 1);
+    const size_t off = ((size_t)row * d.G + g) * SN + (q & 15) * 8;
+    st.c[k] = *reinterpret_cast<const uint4 *>(Cg + off);
+    st.b[k] = *reinterpret_cast<const uint4 *>(Bg + off);
   }
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-    st.x[k] = *reinterpret_cast<const uint4 *>(xg + rowX + (wave + 4 * k) * 8);
-  st.dt = dtg[(size_t)row * d.H + h];
+  {
+    const int row = t0 + min(tid >> 3, len - 1);
+    st.x = *reinterpret_cast<const uint4 *>(xg + ((size_t)row * d.H + h) * SP + (tid & 7) * 8);
+  }
+  st.dt = dtg[(size_t)(t0 + min(lane, len - 1)) * d.H + h];
 }
 
-// Write 8 bf16 of token `lane` (elements col8..col8+7 of its row) transposed
-// into dst[(col8 + j) * LDT + token]; the partner lane holds the other token of
-// the pair.
-__device__ __forceinline__ void transpose_store(bf16_t *dst, int col8, uint4 v, int lane) {
-  const int odd = lane & 1;
-  // v.{x,y,z,w} hold element pairs (0,1) (2,3) (4,5) (6,7).  The even lane keeps
-  // the even elements of each pair and receives the partner's even elements;
-  // the odd lane the odd ones.
-  uint32_t mine[4] = {v.x, v.y, v.z, v.w};
-  uint32_t out[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t send = odd ? (mine[i] & 0xffffu) : (mine[i] >> 16);
-    // swap with the adjacent lane (DPP quad_perm [1,0,3,2])
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-    // word for (token pair, element 2i + odd): low half = even token, high = odd token
-    out[i] = odd ? (recv | (mine[i] & 0xffff0000u)) : ((mine[i] & 0xffffu) | (recv << 16));
-  }
-  const int tok0 = lane & ~1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint32_t *>(dst + (col8 + 2 * i + odd) * LDT + tok0) = out[i];
+// Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 within each
+// 16-lane row, then row 15's and row 31's totals broadcast forward.
+__device__ __forceinline__ float scan64(float v) {
+  const int z = 0;
+#define SSD_SHR(ctrl, rmask)                                                               \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), ctrl, rmask, 0xF, true))
+  SSD_SHR(0x111, 0xF);  // row_shr:1
+  SSD_SHR(0x112, 0xF);  // row_shr:2
+  SSD_SHR(0x114, 0xF);  // row_shr:4
+  SSD_SHR(0x118, 0xF);  // row_shr:8
+  SSD_SHR(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+  SSD_SHR(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+#undef SSD_SHR
+  return v;
 }
 
 __device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
   return ok ? v : make_uint4(0, 0, 0, 0);
 }
-__device__ __forceinline__ void stage_store(const Staged &st, Smem &sm, int len, int lane,
-                                            int wave) {
-  const bool ok = lane < len;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c8 = (wave + 4 * k) * 8;
-    const uint4 b = keep_if(ok, st.b[k]);
-    *reinterpret_cast<uint4 *>(sm.C + sw128(lane, c8)) = keep_if(ok, st.c[k]);
-    *reinterpret_cast<uint4 *>(sm.R + sw128(lane, c8)) = b;
-    transpose_store(sm.BT, c8, b, lane);
+__device__ __forceinline__ uint32_t scale2(uint32_t v, float w) {
+  return pack2_bf16(__uint_as_float(v << 16) * w, __uint_as_float(v & 0xffff0000u) * w);
+}
+
+// Write a staged block to LDS, with its running sums: cs (inclusive sum of
+// dt*A), exp(cs), the G3 weights w_s = exp(cs_end - cs_s) dt_s (applied to x
+// rows here) and lam = exp(cs_end).  Every wave computes the sums (one token
+// per lane); wave 0 publishes them.
+__device__ __forceinline__ void stage_store(const Staged &st, Smem &sm, int len, int tid,
+                                            int lane, int wave, float Ah) {
+  const float dtv = lane < len ? __uint_as_float(st.dt << 16) : 0.f;
+  const float v = scan64(dtv * Ah);
+  // rows past len add nothing, so lane 63 holds the block's total
+  const float end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  const float w = __expf(end - v) * dtv;
+  if (wave == 0) {
+    sm.cs[lane] = v;
+    sm.ecs[lane] = __expf(v);
+    sm.dt[lane] = dtv;
+    if (lane == 0) sm.lam = __expf(end);
   }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) transpose_store(sm.Xt, (wave + 4 * k) * 8, keep_if(ok, st.x[k]), lane);
-  if (wave == 0) sm.dt[lane] = ok ? __uint_as_float(st.dt << 16) : 0.f;
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + kSsdThreads * k;
+    const int row = q >> 4, col = (q & 15) * 8;
+    const bool ok = row < len;
+    *reinterpret_cast<uint4 *>(sm.C + sw_n(row, col)) = keep_if(ok, st.c[k]);
+    *reinterpret_cast<uint4 *>(sm.B + sw_n(row, col)) = keep_if(ok, st.b[k]);
+  }
+  {
+    const int row = tid >> 3, col = (tid & 7) * 8;
+    const uint4 xv = keep_if(row < len, st.x);
+    const float wr = __shfl(w, row);  // zero past len
+    *reinterpret_cast<uint4 *>(sm.X + sw_x(row, col)) = xv;
+    *reinterpret_cast<uint4 *>(sm.XW + sw_x(row, col)) =
+        make_uint4(scale2(xv.x, wr), scale2(xv.y, wr), scale2(xv.z, wr), scale2(xv.w, wr));
+  }
 }
 
 // end (exclusive) of the block starting at t0: Q tokens, the segment end, or
@@ -206,7 +267,7 @@ __device__ __forceinline__ int block_end(const ScanArgs &a, const ScanMeta &m, i
   return t1;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void scan_ssd_kernel(ScanArgs a, ScanMeta m) {
+__global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, ScanMeta m) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -218,143 +279,113 @@ __global__ __launch_bounds__(kThreads, 2) void scan_ssd_kernel(ScanArgs a, ScanM
   const float Ah = a.A[h], Dh = a.D[h];
   bf16_t *yg = (bf16_t *)a.y;
   const size_t PN = (size_t)SP * SN;
-  bf16_t *MT = sm.R;              // [t][s], valid after G1
-  bf16_t *XwT = sm.R + Q * LDT;   // [p][s], valid after G1
 
-  f32x16_t hacc[2];
+  // Accumulators by role: waves 4-7 keep their state tiles (n in [32 nt, +32),
+  // both p tiles) in acc[0..1] for the whole segment, and waves 4-6 build a
+  // masked (C.B)^T tile in acc[2]; waves 0-3 build their y tile in acc[0].
+  const bool swave = wave >= 4;
+  const int nt = wave & 3;
+  f32x16_t acc[3];
+  f32x16_t *hacc = acc;
+  f32x16_t &tile = acc[0], &mt = acc[2];
   bool have_h = sg.init != 0;
-  if (have_h) {
-    state_load(hacc, a.state + (size_t)h * PN, wave, l32, hi);
-    state_to_lds(hacc, sm.HT, wave, l32, hi);
-  } else {
-    hacc[0] = zero16();
-    hacc[1] = zero16();
+  acc[0] = zero16();
+  acc[1] = zero16();
+  if (have_h && swave) {
+    state_load(hacc, a.state + (size_t)h * PN, nt, l32, hi);
+    state_to_lds(hacc, sm.HT, nt, l32, hi);
   }
   int ck = 0;
   while (ck < a.n_ck && m.ck_t[ck] < sg.t0) ++ck;
 
-  // the wave's output tile of y: rows t in [32*ta, +32), columns p in [32*pb, +32)
-  const int ta = wave >> 1, pb = wave & 1;
+  // waves 0-3: y tile rows t in [32 ta, +32), columns p in [32 pb, +32);
+  // waves 4-6: (C.B)^T tile with s in [32 si, +32), t in [32 gt, +32), s <= t
+  const int ta = (wave >> 1) & 1, pb = wave & 1;
+  const bool g1 = wave >= 4 && wave < 7;
+  const int si = wave == 6 ? 1 : 0, gt = wave == 4 ? 0 : 1;
 
   Staged st;
   int t0 = sg.t0;
   int t1 = block_end(a, m, t0, sg.t1, ck);
-  stage_load(st, a, t0, t1 - t0, h, g, lane, wave);
-  stage_store(st, sm, t1 - t0, lane, wave);
+  stage_load(st, a, t0, t1 - t0, h, g, tid, lane);
+  stage_store(st, sm, t1 - t0, tid, lane, wave, Ah);
 
   while (true) {
+    // The lane indices are re-derived each block through an opaque zero:
+    // otherwise the compiler hoists every swizzled LDS address out of the loop
+    // and keeps dozens of them in registers, which spills.
+    int opq = 0;
+    asm volatile("" : "+v"(opq));
+    const int tid = threadIdx.x + opq, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int len = t1 - t0;
     // checkpoints at t1 - 1 are consumed by this block
     int ck_next = ck;
     while (ck_next < a.n_ck && m.ck_t[ck_next] == t1 - 1) ++ck_next;
     const int n0 = t1, n1 = n0 < sg.t1 ? block_end(a, m, n0, sg.t1, ck_next) : n0;
-    __syncthreads();  // [A] this block's inputs are in LDS
+    __syncthreads();  // [A] this block's inputs and running sums are in LDS
 
-    if (n1 > n0) stage_load(st, a, n0, n1 - n0, h, g, lane, wave);  // next block, in flight
+    if (n1 > n0) stage_load(st, a, n0, n1 - n0, h, g, tid, lane);  // next block, in flight
 
-    // ---- running log-decay inside the block (one wave, one token per lane)
-    if (wave == 0) {
-      const float dtv = sm.dt[lane];
-      float v = dtv * Ah;
+    if (!swave) {
+      // ---- G4: C h_prev^T tile (ta, pb), rows scaled by exp(cs_t)
+      tile = zero16();
+      if (have_h) {
+        const int tr = 32 * ta + l32, pr = 32 * pb + l32;
+#pragma unroll 4
+        for (int k = 0; k < SN / 16; ++k) {
+          const int col = 16 * k + 8 * hi;
+          tile = mfma(lds8(sm.C + sw_n(tr, col)), lds8(sm.HT + sw_n(pr, col)), tile);
+        }
+        const float *eb = sm.ecs + 32 * ta + 4 * hi;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float u = __shfl_up(v, off);
-        if (lane >= off) v += u;
+        for (int r = 0; r < 16; ++r) tile[r] *= eb[8 * (r >> 2) + (r & 3)];
       }
-      const float end = __shfl(v, 63);
-      sm.cs[lane] = v;
-      sm.ecs[lane] = __expf(v);
-      sm.w[lane] = __expf(end - v) * dtv;
-      if (lane == 0) sm.lam = __expf(end);
-    }
-    __syncthreads();  // [B]
-
-    // ---- G1 and G4 in one K loop.  Wave w's output tile of y has rows
-    // t in [32 ta, +32) and columns p in [32 pb, +32); G1 tiles are given to
-    // the waves whose y rows match their t-tile, so the C fragment (rows t, K = n)
-    // is read once per K step for both contractions:
-    //   G1 (waves 0, 2, 3): (C.B)^T tile (s-tile si, t-tile ta)
-    //   G4 (every wave):    C h_prev^T tile (ta, pb), scaled by exp(cs_t) after
-    const bool g1 = wave != 1;
-    const int si = wave == 3 ? 1 : 0;
-    float mv[16];
-    f32x16_t yacc = zero16();
-    {
-      f32x16_t acc = zero16();
-      const bf16_t *crow = sm.C + (32 * ta + l32) * SN;
-      const bf16_t *brow = sm.R + (32 * si + l32) * SN;
-      const bf16_t *hrow = sm.HT + (32 * pb + l32) * SN;
-      const int xr = l32 & 15;  // swizzle of every row read here (row & 15 == l32 & 15)
+    } else if (g1) {
+      // ---- G1: (C.B)^T tile (si, gt), masked into M
+      mt = zero16();
+      const int tr = 32 * gt + l32, sr = 32 * si + l32;
 #pragma unroll 4
       for (int k = 0; k < SN / 16; ++k) {
-        const int off = ((2 * k + hi) ^ xr) << 3;
-        const bf16x8_t cv = lds8(crow + off);
-        if (g1) acc = mfma(lds8(brow + off), cv, acc);
-        if (have_h) yacc = mfma(cv, lds8(hrow + off), yacc);
+        const int col = 16 * k + 8 * hi;
+        mt = mfma(lds8(sm.B + sw_n(sr, col)), lds8(sm.C + sw_n(tr, col)), mt);
       }
-      if (g1) {
-        const int t = 32 * ta + l32;
-        const float cst = sm.cs[t];
+      const int t = tr;
+      const float cst = sm.cs[t];
+      const int sb = 32 * si + 4 * hi;
+      const float *csb = sm.cs + sb, *dtb = sm.dt + sb;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int s = 32 * si + acc_row(r, hi);
-          // the skip term D x[t] rides on the diagonal: sum_s M[t,s] x[s] then includes it
-          mv[r] = s <= t ? acc[r] * __expf(cst - sm.cs[s]) * sm.dt[s] + (s == t ? Dh : 0.f) : 0.f;
-        }
-      }
-      if (have_h) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) yacc[r] *= sm.ecs[32 * ta + acc_row(r, hi)];
+      for (int r = 0; r < 16; ++r) {
+        const int so = 8 * (r >> 2) + (r & 3), s = sb + so;
+        // Branch-free: above the diagonal the exponent may be large; the clamp
+        // keeps those discarded entries finite, so the product by the 0/1 mask
+        // is exact.  The skip term D x[t] rides on the diagonal, so
+        // sum_s M[t,s] x[s] includes it.
+        const float v = mt[r] * __expf(fminf(cst - csb[so], 80.f)) * dtb[so];
+        mt[r] = v * (s <= t ? 1.f : 0.f) + (s == t ? Dh : 0.f);
       }
     }
-    __syncthreads();  // [C] B row-major no longer needed: R becomes M^T and (w x)^T
+    __syncthreads();  // [C] G4 has read h_prev; G1 has read B and C
 
     if (g1) {
-      const int t = 32 * ta + l32;
+      const int t = 32 * gt + l32;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2 *>(MT + t * LDT + 32 * si + 8 * q + 4 * hi) =
-            pack4(mv[4 * q], mv[4 * q + 1], mv[4 * q + 2], mv[4 * q + 3]);
+        *reinterpret_cast<uint2 *>(sm.MT + sw_m(t, 32 * si + 8 * q + 4 * hi)) =
+            pack4(mt[4 * q], mt[4 * q + 1], mt[4 * q + 2], mt[4 * q + 3]);
     }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int q = tid + kThreads * k;  // 512 chunks of x^T
-      const int p = q >> 3, s0 = (q & 7) * 8;
-      const uint4 v = *reinterpret_cast<const uint4 *>(sm.Xt + p * LDT + s0);
-      const bf16_t *e = reinterpret_cast<const bf16_t *>(&v);
-      uint4 o;
-      uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ow[j] = pack2_bf16(bf16_to_f(e[2 * j]) * sm.w[s0 + 2 * j],
-                           bf16_to_f(e[2 * j + 1]) * sm.w[s0 + 2 * j + 1]);
-      *reinterpret_cast<uint4 *>(XwT + p * LDT + s0) = o;
-    }
-    __syncthreads();  // [D]
+    __syncthreads();  // [D] M is in LDS
 
-    // ---- G2: intra-block part (and the skip term), (M^T)[t, s<=t] x[s, p]
-    const int ksteps = ta == 0 ? 2 : 4;
-    for (int k = 0; k < ksteps; ++k) {
-      const bf16x8_t av = lds8(MT + (32 * ta + l32) * LDT + 16 * k + 8 * hi);
-      const bf16x8_t bv = lds8(sm.Xt + (32 * pb + l32) * LDT + 16 * k + 8 * hi);
-      yacc = mfma(av, bv, yacc);
-    }
-    // ---- G3: h^T <- lam h^T + B^T (w x)  (this wave's n-tile, both p-tiles)
-    const float lam = sm.lam;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) hacc[j][r] *= lam;
-#pragma unroll 2
-      for (int k = 0; k < Q / 16; ++k) {
-        const bf16x8_t av = lds8(sm.BT + (32 * wave + l32) * LDT + 16 * k + 8 * hi);
-        const bf16x8_t bv = lds8(XwT + (32 * j + l32) * LDT + 16 * k + 8 * hi);
-        hacc[j] = mfma(av, bv, hacc[j]);
+    if (!swave) {
+      // ---- G2: intra-block part and the skip term, M[t, s<=t] x[s, p]
+      const int ksteps = ta == 0 ? 2 : 4;
+      const int pcol = 32 * pb + 16 * ((lane >> 4) & 1);
+      for (int k = 0; k < ksteps; ++k) {
+        const bf16x8_t av = lds8(sm.MT + sw_m(32 * ta + l32, 16 * k + 8 * hi));
+        const bf16x8_t bv = ldtr8(sm.X, 16 * k + 8 * hi, pcol, lane, SwX());
+        tile = mfma(av, bv, tile);
       }
-    }
-    // ---- epilogue: the wave's 32 x 32 y tile goes through its own 2 KiB of the
-    // C region (free since barrier C) and leaves as 16-byte row segments.
-    {
+      // ---- epilogue: the wave's 32 x 32 y tile goes through its own 2 KiB of
+      // the C region (free since barrier C) and leaves as 16-byte row segments.
       bf16_t *yt = sm.C + wave * (32 * 32);  // [t][p], 64 bytes per row
       const int odd = lane & 1;
       const uint32_t sel = 0u - (uint32_t)odd;  // all ones on odd lanes
@@ -364,9 +395,9 @@ __global__ __launch_bounds__(kThreads, 2) void scan_ssd_kernel(ScanArgs a, ScanM
         // The even lane keeps row t and the odd lane row t+1; each sends the
         // other row to its partner.  (Bit blends rather than ?: on vector
         // elements, which the compiler would turn into a variable-index extract.)
-        const uint32_t a = __float_as_uint(yacc[2 * i]), b = __float_as_uint(yacc[2 * i + 1]);
-        const uint32_t keep = (a & ~sel) | (b & sel);
-        const uint32_t send = (b & ~sel) | (a & sel);
+        const uint32_t ra = __float_as_uint(tile[2 * i]), rb = __float_as_uint(tile[2 * i + 1]);
+        const uint32_t keep = (ra & ~sel) | (rb & sel);
+        const uint32_t send = (rb & ~sel) | (ra & sel);
         const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
         // low half = column p (even lane's value), high half = column p+1
         const uint32_t lo = (keep & ~sel) | (recv & sel), hiw = (recv & ~sel) | (keep & sel);
@@ -383,20 +414,40 @@ __global__ __launch_bounds__(kThreads, 2) void scan_ssd_kernel(ScanArgs a, ScanM
         if (t < len)
           *reinterpret_cast<uint4 *>(yg + ((size_t)(t0 + t) * d.H + h) * SP + 32 * pb + c * 8) = v;
       }
+    } else {
+      // ---- G3: h^T <- lam h^T + B^T (w x); then the checkpoints and the bf16
+      // copy of h for the next block's G4 (G4 of this block is done: barrier C)
+      const float lam = sm.lam;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hacc[j][r] *= lam;
+      const int grp = 16 * ((lane >> 4) & 1);
+#pragma unroll
+      for (int k = 0; k < Q / 16; ++k) {
+        const int k0 = 16 * k + 8 * hi;
+        const bf16x8_t av = ldtr8(sm.B, k0, 32 * nt + grp, lane, SwN());
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t bv = ldtr8(sm.XW, k0, 32 * j + grp, lane, SwX());
+          hacc[j] = mfma(av, bv, hacc[j]);
+        }
+      }
+      for (int c = ck; c < ck_next; ++c)
+        state_store(hacc, a.ckpt_out + ((size_t)m.ck_idx[c] * d.H + h) * PN, nt, l32, hi);
+      state_to_lds(hacc, sm.HT, nt, l32, hi);
     }
     have_h = true;
-    for (; ck < ck_next; ++ck)
-      state_store(hacc, a.ckpt_out + ((size_t)m.ck_idx[ck] * d.H + h) * PN, wave, l32, hi);
+    ck = ck_next;
     if (n1 <= n0) break;
     __syncthreads();  // [E] every read of this block's LDS is done
-    state_to_lds(hacc, sm.HT, wave, l32, hi);
-    stage_store(st, sm, n1 - n0, lane, wave);
+    stage_store(st, sm, n1 - n0, tid, lane, wave, Ah);
     t0 = n0;
     t1 = n1;
   }
 
-  if (sg.final)
-    state_store(hacc, (sg.final == 1 ? a.state : a.workspace) + (size_t)h * PN, wave, l32, hi);
+  if (sg.final && swave)
+    state_store(hacc, (sg.final == 1 ? a.state : a.workspace) + (size_t)h * PN, nt, l32, hi);
 }
 
 }  // namespace
@@ -404,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_ssd_kernel(ScanArgs a, ScanM
 bool ssd_supported(int io, const Dims &d) { return io == kBF16 && d.P == SP && d.N == SN; }
 
 hipError_t launch_scan_ssd(const ScanArgs &a, const ScanMeta &m, hipStream_t s) {
-  dim3 grid(a.n_seg * a.d.H), block(kThreads);
+  dim3 grid(a.n_seg * a.d.H), block(kSsdThreads);
   hipLaunchKernelGGL(scan_ssd_kernel, grid, block, 0, s, a, m);
   return hipGetLastError();
 }
