@@ -69,12 +69,12 @@ __device__ __forceinline__ int sw_m(int row, int col) {  // 64-wide rows, row re
 
 // 72 KiB: two workgroups per CU.
 struct Smem {
-  bf16_t C[Q * SN];   // C[t][n]
-  bf16_t B[Q * SN];   // B[s][n]
-  bf16_t HT[SP * SN]; // bf16 copy of h_prev[p][n]
-  bf16_t X[Q * SP];   // x[s][p]
-  bf16_t XW[Q * SP];  // w_s x[s][p]
-  bf16_t MT[Q * Q];   // M[t][s] (masked C.B with D on the diagonal)
+  alignas(16) bf16_t C[Q * SN];   // C[t][n]
+  alignas(16) bf16_t B[Q * SN];   // B[s][n]
+  alignas(16) bf16_t HT[SP * SN]; // bf16 copy of h_prev[p][n]
+  alignas(16) bf16_t X[Q * SP];   // x[s][p]
+  alignas(16) bf16_t XW[Q * SP];  // w_s x[s][p]
+  alignas(16) bf16_t MT[Q * Q];   // M[t][s] (masked C.B with D on the diagonal)
   float cs[Q], ecs[Q], dt[Q];
   float lam;
 };
@@ -83,8 +83,23 @@ static_assert(2 * sizeof(Smem) <= 160 * 1024, "two workgroups per CU");
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// LDS vector accesses with their alignment stated: without it the compiler
+// splits a 16-byte store into 4-byte pairs, which conflict on the banks where
+// one 16-byte store would not.
 __device__ __forceinline__ bf16x8_t lds8(const bf16_t *p) {
-  return *reinterpret_cast<const bf16x8_t *>(p);
+  return *static_cast<const bf16x8_t *>(__builtin_assume_aligned(p, 16));
+}
+__device__ __forceinline__ uint4 lds_ld16(const bf16_t *p) {
+  return *static_cast<const uint4 *>(__builtin_assume_aligned(p, 16));
+}
+__device__ __forceinline__ void lds_st16(bf16_t *p, uint4 v) {
+  *static_cast<uint4 *>(__builtin_assume_aligned(p, 16)) = v;
+}
+__device__ __forceinline__ void lds_st8(bf16_t *p, uint2 v) {
+  *static_cast<uint2 *>(__builtin_assume_aligned(p, 8)) = v;
+}
+__device__ __forceinline__ void lds_st4(bf16_t *p, uint32_t v) {
+  *static_cast<uint32_t *>(__builtin_assume_aligned(p, 4)) = v;
 }
 __device__ __forceinline__ s16x4_t ldtr4(const bf16_t *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -110,6 +125,14 @@ struct SwN {
 struct SwX {
   __device__ __forceinline__ int operator()(int r, int c) const { return sw_x(r, c); }
 };
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes a wave with pending global stores (y, checkpoints) wait
+// for all its outstanding loads too -- including the next block's prefetch.
+// No wave reads another wave's global writes inside this kernel.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
@@ -162,8 +185,8 @@ __device__ __forceinline__ void state_to_lds(const f32x16_t hacc[2], bf16_t *HT,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = 32 * j + l32, n = 32 * nt + 8 * q + 4 * hi;
-      *reinterpret_cast<uint2 *>(HT + sw_n(p, n)) =
-          pack4(hacc[j][4 * q], hacc[j][4 * q + 1], hacc[j][4 * q + 2], hacc[j][4 * q + 3]);
+      lds_st8(HT + sw_n(p, n),
+              pack4(hacc[j][4 * q], hacc[j][4 * q + 1], hacc[j][4 * q + 2], hacc[j][4 * q + 3]));
     }
 }
 
@@ -245,16 +268,16 @@ __device__ __forceinline__ void stage_store(const Staged &st, Smem &sm, int len,
     const int q = tid + kSsdThreads * k;
     const int row = q >> 4, col = (q & 15) * 8;
     const bool ok = row < len;
-    *reinterpret_cast<uint4 *>(sm.C + sw_n(row, col)) = keep_if(ok, st.c[k]);
-    *reinterpret_cast<uint4 *>(sm.B + sw_n(row, col)) = keep_if(ok, st.b[k]);
+    lds_st16(sm.C + sw_n(row, col), keep_if(ok, st.c[k]));
+    lds_st16(sm.B + sw_n(row, col), keep_if(ok, st.b[k]));
   }
   {
     const int row = tid >> 3, col = (tid & 7) * 8;
     const uint4 xv = keep_if(row < len, st.x);
     const float wr = __shfl(w, row);  // zero past len
-    *reinterpret_cast<uint4 *>(sm.X + sw_x(row, col)) = xv;
-    *reinterpret_cast<uint4 *>(sm.XW + sw_x(row, col)) =
-        make_uint4(scale2(xv.x, wr), scale2(xv.y, wr), scale2(xv.z, wr), scale2(xv.w, wr));
+    lds_st16(sm.X + sw_x(row, col), xv);
+    lds_st16(sm.XW + sw_x(row, col),
+             make_uint4(scale2(xv.x, wr), scale2(xv.y, wr), scale2(xv.z, wr), scale2(xv.w, wr)));
   }
 }
 
@@ -322,7 +345,7 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
     int ck_next = ck;
     while (ck_next < a.n_ck && m.ck_t[ck_next] == t1 - 1) ++ck_next;
     const int n0 = t1, n1 = n0 < sg.t1 ? block_end(a, m, n0, sg.t1, ck_next) : n0;
-    __syncthreads();  // [A] this block's inputs and running sums are in LDS
+    lds_barrier();  // [A] this block's inputs and running sums are in LDS
 
     if (n1 > n0) stage_load(st, a, n0, n1 - n0, h, g, tid, lane);  // next block, in flight
 
@@ -363,17 +386,14 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
         const float v = mt[r] * __expf(fminf(cst - csb[so], 80.f)) * dtb[so];
         mt[r] = v * (s <= t ? 1.f : 0.f) + (s == t ? Dh : 0.f);
       }
-    }
-    __syncthreads();  // [C] G4 has read h_prev; G1 has read B and C
-
-    if (g1) {
-      const int t = 32 * gt + l32;
+      // M is read only after the next barrier (the previous block's reads of
+      // it ended before barrier A)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2 *>(sm.MT + sw_m(t, 32 * si + 8 * q + 4 * hi)) =
-            pack4(mt[4 * q], mt[4 * q + 1], mt[4 * q + 2], mt[4 * q + 3]);
+        lds_st8(sm.MT + sw_m(t, 32 * si + 8 * q + 4 * hi),
+                pack4(mt[4 * q], mt[4 * q + 1], mt[4 * q + 2], mt[4 * q + 3]));
     }
-    __syncthreads();  // [D] M is in LDS
+    lds_barrier();  // [C] M is in LDS; G4 has read h_prev
 
     if (!swave) {
       // ---- G2: intra-block part and the skip term, M[t, s<=t] x[s, p]
@@ -383,36 +403,6 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
         const bf16x8_t av = lds8(sm.MT + sw_m(32 * ta + l32, 16 * k + 8 * hi));
         const bf16x8_t bv = ldtr8(sm.X, 16 * k + 8 * hi, pcol, lane, SwX());
         tile = mfma(av, bv, tile);
-      }
-      // ---- epilogue: the wave's 32 x 32 y tile goes through its own 2 KiB of
-      // the C region (free since barrier C) and leaves as 16-byte row segments.
-      bf16_t *yt = sm.C + wave * (32 * 32);  // [t][p], 64 bytes per row
-      const int odd = lane & 1;
-      const uint32_t sel = 0u - (uint32_t)odd;  // all ones on odd lanes
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // registers 2i, 2i+1 are rows t, t+1; adjacent lanes are columns p, p+1.
-        // The even lane keeps row t and the odd lane row t+1; each sends the
-        // other row to its partner.  (Bit blends rather than ?: on vector
-        // elements, which the compiler would turn into a variable-index extract.)
-        const uint32_t ra = __float_as_uint(tile[2 * i]), rb = __float_as_uint(tile[2 * i + 1]);
-        const uint32_t keep = (ra & ~sel) | (rb & sel);
-        const uint32_t send = (rb & ~sel) | (ra & sel);
-        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-        // low half = column p (even lane's value), high half = column p+1
-        const uint32_t lo = (keep & ~sel) | (recv & sel), hiw = (recv & ~sel) | (keep & sel);
-        const int t = acc_row(2 * i, hi) + odd;  // even lane: row t, odd lane: row t+1
-        *reinterpret_cast<uint32_t *>(yt + t * 32 + (l32 & ~1)) =
-            pack2_bf16(__uint_as_float(lo), __uint_as_float(hiw));
-      }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int q = lane + 64 * k;  // 128 chunks of 16 bytes
-        const int row = q >> 2, c = q & 3;
-        const uint4 v = *reinterpret_cast<const uint4 *>(yt + row * 32 + c * 8);
-        const int t = 32 * ta + row;
-        if (t < len)
-          *reinterpret_cast<uint4 *>(yg + ((size_t)(t0 + t) * d.H + h) * SP + 32 * pb + c * 8) = v;
       }
     } else {
       // ---- G3: h^T <- lam h^T + B^T (w x); then the checkpoints and the bf16
@@ -439,9 +429,45 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
     }
     have_h = true;
     ck = ck_next;
-    if (n1 <= n0) break;
-    __syncthreads();  // [E] every read of this block's LDS is done
-    stage_store(st, sm, n1 - n0, tid, lane, wave, Ah);
+    const bool more = n1 > n0;
+    lds_barrier();  // [E] every read of this block's LDS is done
+    // The next block's inputs go to LDS first: waiting for the prefetched
+    // loads here must not also wait for this block's y stores, which are only
+    // issued afterwards.
+    if (more) stage_store(st, sm, n1 - n0, tid, lane, wave, Ah);
+    if (!swave) {
+      // ---- epilogue: the wave's 32 x 32 y tile goes through its own 2 KiB of
+      // the M region (free since barrier E; M is next written after barrier A)
+      // and leaves as 16-byte row segments.
+      bf16_t *yt = sm.MT + wave * (32 * 32);  // [t][p], 64 bytes per row
+      const int odd = lane & 1;
+      const uint32_t sel = 0u - (uint32_t)odd;  // all ones on odd lanes
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // registers 2i, 2i+1 are rows t, t+1; adjacent lanes are columns p, p+1.
+        // The even lane keeps row t and the odd lane row t+1; each sends the
+        // other row to its partner.  (Bit blends rather than ?: on vector
+        // elements, which the compiler would turn into a variable-index extract.)
+        const uint32_t ra = __float_as_uint(tile[2 * i]), rb = __float_as_uint(tile[2 * i + 1]);
+        const uint32_t keep = (ra & ~sel) | (rb & sel);
+        const uint32_t send = (rb & ~sel) | (ra & sel);
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+        // low half = column p (even lane's value), high half = column p+1
+        const uint32_t lo = (keep & ~sel) | (recv & sel), hiw = (recv & ~sel) | (keep & sel);
+        const int t = acc_row(2 * i, hi) + odd;  // even lane: row t, odd lane: row t+1
+        lds_st4(yt + t * 32 + (l32 & ~1), pack2_bf16(__uint_as_float(lo), __uint_as_float(hiw)));
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int q = lane + 64 * k;  // 128 chunks of 16 bytes
+        const int row = q >> 2, c = q & 3;
+        const uint4 v = lds_ld16(yt + row * 32 + c * 8);
+        const int t = 32 * ta + row;
+        if (t < len)
+          *reinterpret_cast<uint4 *>(yg + ((size_t)(t0 + t) * d.H + h) * SP + 32 * pb + c * 8) = v;
+      }
+    }
+    if (!more) break;
     t0 = n0;
     t1 = n1;
   }
