@@ -29,9 +29,9 @@
 // where the two half-waves take contraction indices 32 apart (k and k + 32 of
 // each 64-wide K block); accumulator register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4, column l%32.  Operands are read from LDS one float
-// per lane.  Every operand array has an odd row pitch, so both the 32 rows one
-// half-wave reads along K and the two half-waves' rows 32 apart fall on
-// distinct banks of the 64-bank LDS.
+// per lane.  4-byte LDS reads are served 32 lanes per cycle from 32 banks;
+// every operand array has an odd row pitch, so the 32 rows one half-wave reads
+// along K (stride = pitch) fall on 32 distinct banks.
 //
 // exp is taken as exp2 of an fp32 argument scaled by log2(e) in fp64: the
 // argument is rounded to fp32 once, as it would be for expf.

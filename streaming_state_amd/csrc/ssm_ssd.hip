@@ -47,8 +47,11 @@ constexpr int SP = 64;   // head dim
 constexpr int SN = 128;  // state size
 
 // LDS layouts.  Rows are unpadded; 16-byte chunks are XOR-swizzled by row so
-// that both access patterns of a tile are free of bank conflicts on the
-// 64-bank LDS:
+// that both access patterns of a tile are free of bank conflicts.  The LDS
+// serves 256 bytes per cycle to 8- and 16-byte accesses: a 16-byte access is
+// conflict-free when each group of 16 lanes touches 16 distinct 16-byte slots
+// modulo 256 bytes, an 8-byte access (also the transposing read) when each
+// group of 32 lanes touches 32 distinct 8-byte slots (measured on gfx950):
 //  - 256-byte rows (C, B, h: 128 bf16): chunk ^ f(row), f(r) = (r%4)*4 + (r/4)%4.
 //    A 16-row read of one chunk hits 16 distinct chunks (f is a bijection of
 //    0..15); a transposing read covers rows r..r+3 (r % 4 == 0) x 4 chunks of
@@ -75,7 +78,7 @@ struct Smem {
   alignas(16) bf16_t X[Q * SP];   // x[s][p]
   alignas(16) bf16_t XW[Q * SP];  // w_s x[s][p]
   alignas(16) bf16_t MT[Q * Q];   // M[t][s] (masked C.B with D on the diagonal)
-  float cs[Q], ecs[Q], dt[Q];
+  float csl[Q], ecs[Q], dt[Q];  // running sum of dt*A times log2(e); exp of it; dt
   float lam;
 };
 static_assert(2 * sizeof(Smem) <= 160 * 1024, "two workgroups per CU");
@@ -111,11 +114,20 @@ __device__ __forceinline__ s16x4_t ldtr4(const bf16_t *p) {
 // supplies row k0 + 4r + (l%16)/4, columns col0 + 4(l%4) .. +3; the hardware
 // hands lane j element j%4 of the segments of lanes j/4, 4 + j/4, 8 + j/4 and
 // 12 + j/4, i.e. column col0 + j of rows k0 + 4r .. +3.
+// For K rows k0 = 16k + 8(l/32), the swizzles below do not depend on k, so a
+// lane's two addresses are fixed offsets (computed once, by tr_off) plus
+// 16k whole rows.
+struct TrOff {
+  int o0, o1;
+};
 template <typename SW>
-__device__ __forceinline__ bf16x8_t ldtr8(const bf16_t *tile, int k0, int col0, int lane, SW sw) {
-  const int rr = (lane & 15) >> 2, cc = col0 + 4 * (lane & 3);
-  const s16x4_t lo = ldtr4(tile + sw(k0 + rr, cc));
-  const s16x4_t hi = ldtr4(tile + sw(k0 + 4 + rr, cc));
+__device__ __forceinline__ TrOff tr_off(int col0, int lane, SW sw) {
+  const int rr = (lane & 15) >> 2, cc = col0 + 4 * (lane & 3), hk = 8 * (lane >> 5);
+  return TrOff{sw(hk + rr, cc), sw(hk + 4 + rr, cc)};
+}
+__device__ __forceinline__ bf16x8_t ldtr8(const bf16_t *tile, TrOff o) {
+  const s16x4_t lo = ldtr4(tile + o.o0);
+  const s16x4_t hi = ldtr4(tile + o.o1);
   const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
@@ -258,22 +270,23 @@ __device__ __forceinline__ void stage_store(const Staged &st, Smem &sm, int len,
   const float end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
   const float w = __expf(end - v) * dtv;
   if (wave == 0) {
-    sm.cs[lane] = v;
+    sm.csl[lane] = v * 1.4426950408889634f;
     sm.ecs[lane] = __expf(v);
     sm.dt[lane] = dtv;
     if (lane == 0) sm.lam = __expf(end);
   }
+  const bool full = len == Q;  // otherwise rows past len are zeroed
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int q = tid + kSsdThreads * k;
     const int row = q >> 4, col = (q & 15) * 8;
-    const bool ok = row < len;
-    lds_st16(sm.C + sw_n(row, col), keep_if(ok, st.c[k]));
-    lds_st16(sm.B + sw_n(row, col), keep_if(ok, st.b[k]));
+    const bool ok = full || row < len;
+    lds_st16(sm.C + sw_n(row, col), full ? st.c[k] : keep_if(ok, st.c[k]));
+    lds_st16(sm.B + sw_n(row, col), full ? st.b[k] : keep_if(ok, st.b[k]));
   }
   {
     const int row = tid >> 3, col = (tid & 7) * 8;
-    const uint4 xv = keep_if(row < len, st.x);
+    const uint4 xv = full ? st.x : keep_if(row < len, st.x);
     const float wr = __shfl(w, row);  // zero past len
     lds_st16(sm.X + sw_x(row, col), xv);
     lds_st16(sm.XW + sw_x(row, col),
@@ -373,18 +386,25 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
         mt = mfma(lds8(sm.B + sw_n(sr, col)), lds8(sm.C + sw_n(tr, col)), mt);
       }
       const int t = tr;
-      const float cst = sm.cs[t];
+      const float cst = sm.csl[t];
       const int sb = 32 * si + 4 * hi;
-      const float *csb = sm.cs + sb, *dtb = sm.dt + sb;
+      const float *csb = sm.csl + sb, *dtb = sm.dt + sb;
+      if (si != gt) {  // the tile below the diagonal: every s < t
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int so = 8 * (r >> 2) + (r & 3), s = sb + so;
-        // Branch-free: above the diagonal the exponent may be large; the clamp
-        // keeps those discarded entries finite, so the product by the 0/1 mask
-        // is exact.  The skip term D x[t] rides on the diagonal, so
-        // sum_s M[t,s] x[s] includes it.
-        const float v = mt[r] * __expf(fminf(cst - csb[so], 80.f)) * dtb[so];
-        mt[r] = v * (s <= t ? 1.f : 0.f) + (s == t ? Dh : 0.f);
+        for (int r = 0; r < 16; ++r) {
+          const int so = 8 * (r >> 2) + (r & 3);
+          mt[r] *= __builtin_amdgcn_exp2f(cst - csb[so]) * dtb[so];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int so = 8 * (r >> 2) + (r & 3), s = sb + so;
+          // above the diagonal the exponent may overflow: selected away.  The
+          // skip term D x[t] rides on the diagonal, so sum_s M[t,s] x[s]
+          // includes it.
+          const float v = mt[r] * __builtin_amdgcn_exp2f(cst - csb[so]) * dtb[so];
+          mt[r] = s < t ? v : (s == t ? v + Dh : 0.f);
+        }
       }
       // M is read only after the next barrier (the previous block's reads of
       // it ended before barrier A)
@@ -398,10 +418,10 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
     if (!swave) {
       // ---- G2: intra-block part and the skip term, M[t, s<=t] x[s, p]
       const int ksteps = ta == 0 ? 2 : 4;
-      const int pcol = 32 * pb + 16 * ((lane >> 4) & 1);
+      const TrOff xo = tr_off(32 * pb + 16 * ((lane >> 4) & 1), lane, SwX());
       for (int k = 0; k < ksteps; ++k) {
         const bf16x8_t av = lds8(sm.MT + sw_m(32 * ta + l32, 16 * k + 8 * hi));
-        const bf16x8_t bv = ldtr8(sm.X, 16 * k + 8 * hi, pcol, lane, SwX());
+        const bf16x8_t bv = ldtr8(sm.X + 16 * k * SP, xo);
         tile = mfma(av, bv, tile);
       }
     } else {
@@ -413,15 +433,13 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
 #pragma unroll
         for (int r = 0; r < 16; ++r) hacc[j][r] *= lam;
       const int grp = 16 * ((lane >> 4) & 1);
+      const TrOff bo = tr_off(32 * nt + grp, lane, SwN());
+      const TrOff wo0 = tr_off(grp, lane, SwX()), wo1 = tr_off(32 + grp, lane, SwX());
 #pragma unroll
       for (int k = 0; k < Q / 16; ++k) {
-        const int k0 = 16 * k + 8 * hi;
-        const bf16x8_t av = ldtr8(sm.B, k0, 32 * nt + grp, lane, SwN());
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8_t bv = ldtr8(sm.XW, k0, 32 * j + grp, lane, SwX());
-          hacc[j] = mfma(av, bv, hacc[j]);
-        }
+        const bf16x8_t av = ldtr8(sm.B + 16 * k * SN, bo);
+        hacc[0] = mfma(av, ldtr8(sm.XW + 16 * k * SP, wo0), hacc[0]);
+        hacc[1] = mfma(av, ldtr8(sm.XW + 16 * k * SP, wo1), hacc[1]);
       }
       for (int c = ck; c < ck_next; ++c)
         state_store(hacc, a.ckpt_out + ((size_t)m.ck_idx[c] * d.H + h) * PN, nt, l32, hi);
@@ -438,24 +456,16 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
     if (!swave) {
       // ---- epilogue: the wave's 32 x 32 y tile goes through its own 2 KiB of
       // the M region (free since barrier E; M is next written after barrier A)
-      // and leaves as 16-byte row segments.
+      // and leaves as 16-byte row segments.  Registers 2i, 2i+1 hold rows t,
+      // t+1 of column p = l%32: one conversion packs both, written as two
+      // 16-bit halves.
       bf16_t *yt = sm.MT + wave * (32 * 32);  // [t][p], 64 bytes per row
-      const int odd = lane & 1;
-      const uint32_t sel = 0u - (uint32_t)odd;  // all ones on odd lanes
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // registers 2i, 2i+1 are rows t, t+1; adjacent lanes are columns p, p+1.
-        // The even lane keeps row t and the odd lane row t+1; each sends the
-        // other row to its partner.  (Bit blends rather than ?: on vector
-        // elements, which the compiler would turn into a variable-index extract.)
-        const uint32_t ra = __float_as_uint(tile[2 * i]), rb = __float_as_uint(tile[2 * i + 1]);
-        const uint32_t keep = (ra & ~sel) | (rb & sel);
-        const uint32_t send = (rb & ~sel) | (ra & sel);
-        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-        // low half = column p (even lane's value), high half = column p+1
-        const uint32_t lo = (keep & ~sel) | (recv & sel), hiw = (recv & ~sel) | (keep & sel);
-        const int t = acc_row(2 * i, hi) + odd;  // even lane: row t, odd lane: row t+1
-        lds_st4(yt + t * 32 + (l32 & ~1), pack2_bf16(__uint_as_float(lo), __uint_as_float(hiw)));
+        const uint32_t pk = pack2_bf16(tile[2 * i], tile[2 * i + 1]);
+        const int t = acc_row(2 * i, hi);
+        yt[t * 32 + l32] = (bf16_t)pk;
+        yt[(t + 1) * 32 + l32] = (bf16_t)(pk >> 16);
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
