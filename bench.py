@@ -41,8 +41,8 @@ MIB = 1 << 20
 # figure into null until the counters are taken again.
 DECODE_COUNTERS = {
     "sources": ["ssm_kernels.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "cfccd028b9f867ff6c937b67792f88e01115c9f92151808429270fdb0cff1f39",
-    "fetch_kib": 519388.11, "write_kib": 1056783.73,
+    "sha256": "cbb0bbe7cfe7f70359edf055d20c161e34b86e78b5f8f45f8ba4420a67f60286",
+    "fetch_kib": 519387.49, "write_kib": 1056784.21,
     "calib_fetch_kib": 2059.01, "calib_write_kib": 4096.0, "calib_true_kib": 4096.0,
     "algorithmic_kib": 1035989.33 + 1056768.0,
 }
@@ -408,9 +408,14 @@ def cpu_baseline(inputs, dec_in, dec_reset, A, D, Bd, H, P, N, G, seconds, torch
     pos = np.zeros(Bd, np.int64)
     slots = np.arange(Bd, dtype=np.int32)
     done, bytes_, t_used = 0, 0.0, 0.0
-    while t_used < seconds and done < len(dec_in):
-        x, dt, B, C = (t.cpu().numpy() for t in dec_in[done])
-        reset = dec_reset[done]
+    host_in = {}
+    # cycle through the workload's decode steps until the time budget is used
+    while t_used < seconds and done < 100000:
+        i = done % len(dec_in)
+        if i not in host_in:
+            host_in[i] = tuple(t.cpu().numpy() for t in dec_in[i])
+        x, dt, B, C = host_in[i]
+        reset = dec_reset[i]
         t0 = time.perf_counter()
         oracle.decode(state, pos, slots, x, dt, B, C, A, D, reset=reset, n_threads=cores)
         t_used += time.perf_counter() - t0
@@ -429,7 +434,8 @@ def cpu_baseline(inputs, dec_in, dec_reset, A, D, Bd, H, P, N, G, seconds, torch
         pass
     return {"value": round(bytes_ / t_used / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{done} full decode steps (256 slots x 128 heads, fp64) in {t_used:.1f} s; "
+            "sample": f"{done} full decode steps (256 slots x 128 heads, fp64; the workload's "
+                      f"{len(dec_in)} step inputs cycled) in {t_used:.1f} s; "
                       f"fp32-equivalent state bytes; {model}; {platform.machine()}"}
 
 
