@@ -189,6 +189,22 @@ def main():
     pre_seq = [0]
     flushes_before = 0
 
+    rep_bytes = []
+    entry_b = (H + H * P + G * N) * 4   # one log entry: dt[H], x[H,P], B[G,N]
+    io_b = n_in * (2 * H * P + H + 2 * G * N) * 4  # in-flight x, dt, B, C in; y out
+
+    def replay_bytes(r, slots, W):
+        """Checkpoint read; on a fold, the committed log read and the checkpoint
+        written; otherwise the committed log read for the outputs; the n_in
+        in-flight entries appended; in-flight inputs and outputs."""
+        tot = 0
+        for b in slots:
+            ln = r.log_state(int(b))[0]
+            tot += state_b + ln * entry_b + n_in * entry_b + io_b
+            if ln + n_in > W:
+                tot += state_b
+        return tot
+
     def one_step(s, timed):
         i = s % n_dec_inputs
         if want("decode"):
@@ -202,6 +218,8 @@ def main():
         a = acc_all[s % len(acc_all)]
         sp = spec_in[s % len(spec_in)]
         if rep16 is not None:
+            if timed:  # algorithmic bytes of this verify step, from the log lengths
+                rep_bytes.append(replay_bytes(rep16, slots3, 16))
             e = t_rep.start() if timed else None
             rep16.replay_step(slots3, *sp, y=y_spec)
             if timed:
@@ -247,7 +265,9 @@ def main():
     if rep16 is not None:
         ms = np.array(t_rep.ms())
         comp["replay_W16"] = dict(ms_mean=float(ms.mean()), ms_median=float(np.median(ms)),
-                                  flushes=int(rep16.counters()["replay_flushes"] - flushes_before))
+                                  flushes=int(rep16.counters()["replay_flushes"] - flushes_before),
+                                  bytes_per_step=float(np.mean(rep_bytes)),
+                                  GBps=float(np.mean(rep_bytes) / (ms.mean() * 1e-3) / 1e9))
     if cop is not None:
         ms = np.array(t_cop.ms())
         cbytes = Bd * state_b * (1 + n_in) + Bd * n_in * (H * P * 8 + H * 4 + 2 * G * N * 4)
@@ -317,6 +337,7 @@ def main():
                                        us_per_call=gpu_ms * 1e3 / len(sizes),
                                        host_wall_us_per_call=wall1 * 1e6 / len(sizes))
         extras["stream_130m"] = stream1
+        extras["replay_alone_vs_decode"] = replay_alone_sweep(torch, ssm, inputs, H, P, N, G, dev)
         # plain device copy of 1 GiB for the achievable-bandwidth context
         a = torch.empty(256 * MIB, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -375,6 +396,54 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
+
+
+def replay_alone_sweep(torch, ssm, inputs, H, P, N, G, dev, W=16, steps=32, warm=16):
+    """ReplaySSM with one token per step (no drafts) against plain decode on the
+    same inputs, per batch size: mean step time of each over `steps` steps after
+    `warm` (two full windows, so the fold every W steps is included).  State
+    traffic per token: decode reads and writes the state, replay reads the
+    checkpoint and writes it once per window."""
+    A, D = inputs.params(2, H)
+    At, Dt = torch.from_numpy(A).to(dev), torch.from_numpy(D).to(dev)
+    out = {}
+    for Bs in (1, 16, 64, 128, 256, 512):
+        init = inputs.device_state(2, Bs, H, P, N)
+        dec = ssm.StreamState(H, P, N, Bs, At, Dt, G=G)
+        rep = ssm.StreamState(H, P, N, Bs, At, Dt, G=G)
+        dec.init(np.arange(Bs), init)
+        rep.init(np.arange(Bs), init)
+        rep.replay_attach(W)
+        del init
+        toks = [inputs.device_tokens(2, Bs, H, P, N, G, seed_extra=500 + s) for s in range(4)]
+        slots = np.arange(Bs, dtype=np.int32)
+        ones = np.ones(Bs, np.int32)
+        yd = torch.empty((Bs, H, P), dtype=torch.float32, device=dev)
+        yr = torch.empty((Bs, 1, H, P), dtype=torch.float32, device=dev)
+        td, tr = Timer(torch), Timer(torch)
+        for i in range(warm + steps):
+            x, dt, B, C = toks[i % len(toks)]
+            e = td.start() if i >= warm else None
+            dec.decode_step(slots, x, dt, B, C, y=yd)
+            if e is not None:
+                td.stop(e)
+            e = tr.start() if i >= warm else None
+            rep.replay_step(slots, x.view(Bs, 1, H, P), dt.view(Bs, 1, H), B.view(Bs, 1, G, N),
+                            C.view(Bs, 1, G, N), y=yr)
+            if e is not None:
+                tr.stop(e)
+            rep.replay_commit(slots, ones)
+        torch.cuda.synchronize()
+        md, mr = float(np.mean(td.ms())), float(np.mean(tr.ms()))
+        st = Bs * H * P * N * 4
+        out[str(Bs)] = dict(decode_ms=md, replay_ms=mr, speedup=md / mr,
+                            decode_state_GBps=2 * st / (md * 1e-3) / 1e9,
+                            replay_state_GBps=st * (1 + 1 / W) / (mr * 1e-3) / 1e9)
+        dec.destroy()
+        rep.destroy()
+        del dec, rep, toks, yd, yr
+    out["model_state_traffic_ratio"] = 2 / (1 + 1 / W)
+    return out
 
 
 def calib_copy(torch, ssm, args):

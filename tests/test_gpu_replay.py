@@ -29,6 +29,7 @@ def ssm():
     (8, 1, 2, 64, 128, 1, "f32"),   # one token per step: the plain-decode case
     (16, 5, 2, 64, 128, 1, "bf16"),
     (5, 5, 2, 16, 32, 1, "f32"),    # every step flushes a full window
+    (64, 16, 2, 64, 128, 1, "f32"),  # the largest window and in-flight count (>64 KiB LDS)
 ])
 def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io):
     S, b, steps = 6, 4, 40
@@ -115,3 +116,45 @@ def test_replay_workload3_full_batch(ssm, W):
     h.materialize(slots)
     assert_close(host(h.state[idx]), ref_state, what="state", **F32_TOL)
     h.destroy()
+
+
+def test_replay_alone_matches_decode(ssm):
+    """One token per step through ReplaySSM (no drafts, W=16) against plain
+    decode on the same inputs: equal outputs every step, and after the log is
+    folded back the same state, over 40 steps (two folds).  Both also agree
+    with the oracle's decode."""
+    S, H, P, N, G, W, steps = 12, 3, 64, 128, 1, 16, 40
+    say("replay alone vs decode", S, H, P, N, W, steps)
+    A, D = inputs.params(2, H)
+    r = np.random.default_rng(7)
+    st0 = (r.standard_normal((S, H, P, N)) * 0.05).astype(np.float32)
+    dec = ssm.StreamState(H, P, N, S, to_dev(A), to_dev(D), G=G)
+    rep = ssm.StreamState(H, P, N, S, to_dev(A), to_dev(D), G=G)
+    slots = np.arange(S, dtype=np.int32)
+    dec.init(slots, to_dev(st0))
+    rep.init(slots, to_dev(st0))
+    rep.replay_attach(W)
+    ref_state = st0.astype(np.float64)
+    ref_pos = np.zeros(S, np.int64)
+    ones = np.ones(S, np.int32)
+    for step in range(steps):
+        x, dt, B, C = inputs.tokens(33, S, H, P, N, G, step)
+        dev = [to_dev(a) for a in (x, dt, B, C)]
+        yd = dec.decode_step(slots, *dev)
+        yr = rep.replay_step(slots, dev[0][:, None], dev[1][:, None], dev[2][:, None],
+                             dev[3][:, None])
+        rep.replay_commit(slots, ones)
+        ref = oracle.decode(ref_state, ref_pos, slots, x, dt, B, C, A, D)
+        torch.cuda.synchronize()
+        assert_close(host(yr[:, 0]), host(yd), what=f"replay vs decode step {step}", **F32_TOL)
+        assert_close(host(yd), ref, what=f"decode vs oracle step {step}", **F32_TOL)
+    # the log fills after W steps: the folds come before steps W and 2W
+    assert rep.counters()["replay_flushes"] == 2 * S
+    rep.materialize(slots)
+    torch.cuda.synchronize()
+    assert_close(host(rep.state), host(dec.state), what="materialized state", **F32_TOL)
+    assert_close(host(dec.state), ref_state, what="state vs oracle", **F32_TOL)
+    for b in range(S):
+        assert rep.position(b)[0] == dec.position(b)[0] == steps
+    dec.destroy()
+    rep.destroy()
