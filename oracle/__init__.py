@@ -8,7 +8,8 @@ HIP library (``streaming_state_amd``); neither imports the other.
 ``ssm_oracle.c`` holds the recurrence (plain sequential fp64 loops); this
 module only marshals numpy arrays into it.  ``acceptance.py`` and
 ``schedule.py`` hold the integer/host-side model of speculative decoding and
-of the replay flush schedule.
+of the replay flush schedule; ``blob.py`` reads and writes the state-blob byte
+format of the recurrent-state companion store.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against the pages and
 the mathematics (worked example, closed forms, brute force); none is "parity
