@@ -274,6 +274,39 @@ ssm_status ssm_state_checkpoint(ssm_handle h, int32_t slot, float *d_dst, ssm_re
 ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
                              const ssm_receipt *r, void *stream);
 
+/* ------------------------------------------------------------- state blobs */
+
+/* Bytes of the blob ssm_state_serialize writes for this layer: 28 + 4*H*P*N,
+ * or 0 for an invalid desc.  The format is the reference serialization of the
+ * recurrent-state companion store ("SSM.PREFIX.* -- recurrent-state
+ * companion"): u32 version = 1, u32 n_arrays, then per array u32 ndim, u32
+ * shape[ndim], u32 dtype_code (0 fp32, 1 fp16, 2 bf16 carried as fp32) and the
+ * raw element bytes, all little-endian. */
+size_t ssm_blob_bytes(const ssm_layer_desc *desc);
+
+/* Checkpoint `slot` into a host blob: materialize it, write one fp32 array of
+ * shape [H, P, N] (dtype code 0) into h_blob (caller-owned host memory of
+ * `cap` bytes; SSM_E_INVALID_ARG if cap < ssm_blob_bytes), set *written and
+ * fill *out as ssm_state_checkpoint does.  The blob carries only the state;
+ * the receipt travels beside it.  Synchronises `stream`. */
+ssm_status ssm_state_serialize(ssm_handle h, int32_t slot, void *h_blob, size_t cap,
+                               size_t *written, ssm_receipt *out, void *stream);
+
+/* Resume `slot` from a host blob of `len` bytes and its receipt (the
+ * section "Make reset, checkpoint, and cancellation observable" of "Mamba
+ * Streaming State That Survives Chunking": a resume that does not match is
+ * refused).  The blob may hold several arrays; the state is the last one
+ * (a Mamba blob is [conv_state, ssm_state]), of shape [H, P, N] after any
+ * leading extents of 1, with dtype code 0 or 2 (fp32 words; for code 2 every
+ * word must be a bf16 value) or 1 (fp16, widened exactly).  SSM_E_SCHEMA,
+ * with the slot unchanged, for a malformed blob (wrong version, truncated,
+ * trailing bytes, unknown dtype code), a state array of the wrong shape, a
+ * receipt that does not match the handle, or a checksum (taken over the
+ * widened fp32 words) that does not match the receipt.  The slot takes the
+ * receipt's stream id, position and chunk sequence.  Synchronises `stream`. */
+ssm_status ssm_state_deserialize(ssm_handle h, int32_t slot, const void *h_blob, size_t len,
+                                 const ssm_receipt *r, void *stream);
+
 /* Read a slot's position and next expected chunk sequence number. */
 ssm_status ssm_get_position(ssm_handle h, int32_t slot, int64_t *pos, uint64_t *chunk_seq);
 

@@ -880,6 +880,35 @@ ssm_status ssm_state_checkpoint(ssm_handle h, int32_t slot, float *d_dst, ssm_re
   return SSM_OK;
 }
 
+namespace {
+
+// A receipt field that does not match the handle, or nullptr.
+static const char *receipt_mismatch(const Handle *H, const ssm_receipt *r) {
+  if (r->schema_version != H->desc.schema_version) return "schema version";
+  if (r->state_dtype != SSM_F32) return "state dtype";
+  if (r->H != H->d.H || r->P != H->d.P || r->N != H->d.N || r->G != H->d.G) return "dimensions";
+  if (r->model_rev != H->desc.model_rev) return "model revision";
+  if (r->code_rev != kCodeRev) return "code revision";
+  if (r->position < 0) return "position";
+  return nullptr;
+}
+
+// The slot continues the stream the receipt names: its position, chunk
+// sequence and id; no replay log and no live copy.
+static void adopt_receipt(Handle *H, int slot, const ssm_receipt *r) {
+  Slot &sl = H->slots[slot];
+  sl.pos = r->position;
+  sl.chunk_seq = r->chunk_seq;
+  sl.stream_id = r->stream_id;
+  sl.log_len = 0;
+  sl.live = -1;
+  sl.pend = kNone;
+  H->cnt.restores++;
+  H->cnt.state_bytes_written += H->state_bytes();
+}
+
+}  // namespace
+
 ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
                              const ssm_receipt *r, void *stream) {
   GET_HANDLE(H, h);
@@ -888,14 +917,7 @@ ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
     return fail(SSM_E_INVALID_ARG, "restore: NULL or misaligned source, or NULL receipt");
   if (H->slots[slot].pend != kNone)
     return fail(SSM_E_LOG, "restore: slot %d has a verify step awaiting commit", slot);
-  const char *bad = nullptr;
-  if (r->schema_version != H->desc.schema_version) bad = "schema version";
-  else if (r->state_dtype != SSM_F32) bad = "state dtype";
-  else if (r->H != H->d.H || r->P != H->d.P || r->N != H->d.N || r->G != H->d.G) bad = "dimensions";
-  else if (r->model_rev != H->desc.model_rev) bad = "model revision";
-  else if (r->code_rev != kCodeRev) bad = "code revision";
-  else if (r->position < 0) bad = "position";
-  if (bad) {
+  if (const char *bad = receipt_mismatch(H, r)) {
     H->cnt.restores_rejected++;
     return fail(SSM_E_SCHEMA, "restore: receipt %s does not match the handle", bad);
   }
@@ -908,15 +930,219 @@ ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
     return fail(SSM_E_SCHEMA, "restore: checksum mismatch (state does not match its receipt)");
   }
   HIP_TRY(launch_copy_f32(H->slot_state(slot), d_src, H->state_bytes() / 4, s));
-  Slot &sl = H->slots[slot];
-  sl.pos = r->position;
-  sl.chunk_seq = r->chunk_seq;
-  sl.stream_id = r->stream_id;
-  sl.log_len = 0;
-  sl.live = -1;
-  sl.pend = kNone;
-  H->cnt.restores++;
-  H->cnt.state_bytes_written += H->state_bytes();
+  adopt_receipt(H, slot, r);
+  return SSM_OK;
+}
+
+// ------------------------------------------------------------- state blobs
+// The byte format of the recurrent-state companion store ("SSM.PREFIX.* --
+// recurrent-state companion", its reference serialization format): a u32
+// version (1) and a u32 array count, then per array a u32 rank, the u32
+// extents, a u32 dtype code (0 fp32, 1 fp16, 2 bf16 widened to fp32) and the
+// raw element bytes.  Every u32 and element is little-endian.
+static_assert(__BYTE_ORDER__ == __ORDER_LITTLE_ENDIAN__, "blob payloads are copied as host words");
+
+namespace {
+
+constexpr uint32_t kBlobVersion = 1;
+constexpr uint32_t kBlobMaxRank = 16;
+constexpr uint32_t kBlobF32 = 0, kBlobF16 = 1, kBlobBF16 = 2;
+
+static size_t blob_size(const Dims &d) {
+  return 8 + 4 + 3 * 4 + 4 + (size_t)d.H * d.P * d.N * sizeof(float);
+}
+
+static void put_u32(uint8_t *p, uint32_t v) {
+  for (int i = 0; i < 4; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+static uint32_t get_u32(const uint8_t *p) {
+  return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+}
+
+// The receipt's checksum, taken on the host.
+static uint64_t host_checksum(const float *v, size_t n) {
+  uint64_t sum = 0;
+  for (size_t i = 0; i < n; ++i) {
+    uint32_t w;
+    memcpy(&w, v + i, 4);
+    sum += (uint64_t)w * (2ull * i + 1ull);
+  }
+  return sum;
+}
+
+// IEEE 754 binary16 to binary32.  Every binary16 value is exact in binary32;
+// subnormals (m * 2^-24) go through ldexpf, which is exact for them.
+static float half_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+  uint32_t bits;
+  if (e == 0x1fu) {
+    bits = sign | 0x7f800000u | (m << 13);  // infinity, NaN keeps its payload
+  } else if (e != 0) {
+    bits = sign | ((e + 127u - 15u) << 23) | (m << 13);
+  } else {
+    const float mag = ldexpf((float)m, -24);
+    memcpy(&bits, &mag, 4);
+    bits |= sign;
+  }
+  float f;
+  memcpy(&f, &bits, 4);
+  return f;
+}
+
+struct BlobArray {
+  std::vector<uint32_t> shape;
+  uint32_t dtype = 0;
+  const uint8_t *data = nullptr;
+  size_t count = 0;
+};
+
+// Walk a blob with every length checked against `len`; nullptr on success,
+// else what is wrong.  Trailing bytes after the last array are an error.
+static const char *parse_blob(const uint8_t *p, size_t len, std::vector<BlobArray> *out) {
+  size_t at = 0;
+  auto have = [&](size_t n) { return n <= len - at; };
+  if (!have(8)) return "shorter than its header";
+  if (get_u32(p) != kBlobVersion) return "version is not 1";
+  const uint32_t n_arrays = get_u32(p + 4);
+  at = 8;
+  if (n_arrays == 0) return "holds no arrays";
+  if (n_arrays > (len - at) / 8) return "array count exceeds its length";
+  out->clear();
+  for (uint32_t a = 0; a < n_arrays; ++a) {
+    BlobArray arr;
+    if (!have(4)) return "truncated in an array header";
+    const uint32_t rank = get_u32(p + at);
+    at += 4;
+    if (rank > kBlobMaxRank) return "array rank above 16";
+    if (!have((size_t)rank * 4 + 4)) return "truncated in an array header";
+    size_t count = 1;
+    for (uint32_t k = 0; k < rank; ++k) {
+      const uint32_t ext = get_u32(p + at);
+      at += 4;
+      arr.shape.push_back(ext);
+      if (ext != 0 && count > SIZE_MAX / 4 / ext) return "array size overflows";
+      count *= ext;
+    }
+    arr.dtype = get_u32(p + at);
+    at += 4;
+    if (arr.dtype > kBlobBF16) return "unknown dtype code";
+    const size_t bytes = count * (arr.dtype == kBlobF16 ? 2 : 4);
+    if (!have(bytes)) return "truncated in array data";
+    arr.data = p + at;
+    arr.count = count;
+    at += bytes;
+    out->push_back(std::move(arr));
+  }
+  if (at != len) return "has trailing bytes after its last array";
+  return nullptr;
+}
+
+}  // namespace
+
+size_t ssm_blob_bytes(const ssm_layer_desc *desc) {
+  if (check_desc(desc) != SSM_OK) return 0;
+  return blob_size(dims_of(desc));
+}
+
+ssm_status ssm_state_serialize(ssm_handle h, int32_t slot, void *h_blob, size_t cap,
+                               size_t *written, ssm_receipt *out, void *stream) {
+  GET_HANDLE(H, h);
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "serialize: bad slot %d", slot);
+  if (!h_blob || !written || !out)
+    return fail(SSM_E_INVALID_ARG, "serialize: NULL blob, length or receipt pointer");
+  const size_t need = blob_size(H->d);
+  if (cap < need)
+    return fail(SSM_E_INVALID_ARG, "serialize: blob capacity %zu below the %zu bytes needed", cap,
+                need);
+  if (H->slots[slot].pend != kNone)
+    return fail(SSM_E_LOG, "serialize: slot %d has a verify step awaiting commit", slot);
+  hipStream_t s = as_stream(stream);
+  const int32_t one = slot;
+  ssm_status st = materialize(H, 1, &one, s);
+  if (st != SSM_OK) return st;
+  // Bounce through an aligned host buffer: the payload sits 28 bytes into the blob.
+  const size_t nf = H->state_bytes() / 4;
+  std::vector<float> host(nf);
+  HIP_TRY(hipMemcpyAsync(host.data(), H->slot_state(slot), H->state_bytes(),
+                         hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  uint8_t *b = static_cast<uint8_t *>(h_blob);
+  const uint32_t head[7] = {kBlobVersion, 1u, 3u, (uint32_t)H->d.H, (uint32_t)H->d.P,
+                            (uint32_t)H->d.N, kBlobF32};
+  for (int i = 0; i < 7; ++i) put_u32(b + 4 * i, head[i]);
+  memcpy(b + 28, host.data(), H->state_bytes());
+  *written = need;
+  const Slot &sl = H->slots[slot];
+  ssm_receipt r{};
+  r.stream_id = sl.stream_id;
+  r.model_rev = H->desc.model_rev;
+  r.code_rev = kCodeRev;
+  r.schema_version = H->desc.schema_version;
+  r.state_dtype = SSM_F32;
+  r.H = H->d.H;
+  r.P = H->d.P;
+  r.N = H->d.N;
+  r.G = H->d.G;
+  r.position = sl.pos;
+  r.chunk_seq = sl.chunk_seq;
+  r.checksum = host_checksum(host.data(), nf);
+  *out = r;
+  H->cnt.checkpoints++;
+  H->cnt.state_bytes_read += H->state_bytes();
+  return SSM_OK;
+}
+
+ssm_status ssm_state_deserialize(ssm_handle h, int32_t slot, const void *h_blob, size_t len,
+                                 const ssm_receipt *r, void *stream) {
+  GET_HANDLE(H, h);
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "deserialize: bad slot %d", slot);
+  if (!h_blob || !r) return fail(SSM_E_INVALID_ARG, "deserialize: NULL blob or receipt");
+  if (H->slots[slot].pend != kNone)
+    return fail(SSM_E_LOG, "deserialize: slot %d has a verify step awaiting commit", slot);
+  auto reject = [&](const char *what) {
+    H->cnt.restores_rejected++;
+    return fail(SSM_E_SCHEMA, "deserialize: blob %s", what);
+  };
+  if (const char *bad = receipt_mismatch(H, r)) {
+    H->cnt.restores_rejected++;
+    return fail(SSM_E_SCHEMA, "deserialize: receipt %s does not match the handle", bad);
+  }
+  std::vector<BlobArray> arrays;
+  if (const char *bad = parse_blob(static_cast<const uint8_t *>(h_blob), len, &arrays))
+    return reject(bad);
+  // The recurrent state is the last array (a Mamba blob is [conv_state, ssm_state]);
+  // its extents are [H, P, N], optionally after leading extents of 1.
+  const BlobArray &a = arrays.back();
+  const size_t rank = a.shape.size();
+  bool shape_ok = rank >= 3 && a.shape[rank - 3] == (uint32_t)H->d.H &&
+                  a.shape[rank - 2] == (uint32_t)H->d.P && a.shape[rank - 1] == (uint32_t)H->d.N;
+  for (size_t k = 0; shape_ok && k + 3 < rank; ++k) shape_ok = a.shape[k] == 1;
+  if (!shape_ok) return reject("state array is not [H, P, N] for this handle");
+  const size_t nf = a.count;
+  std::vector<float> host(nf);
+  if (a.dtype == kBlobF16) {
+    for (size_t i = 0; i < nf; ++i)
+      host[i] = half_to_float((uint16_t)(a.data[2 * i] | a.data[2 * i + 1] << 8));
+  } else {
+    memcpy(host.data(), a.data, nf * 4);
+    if (a.dtype == kBlobBF16)
+      for (size_t i = 0; i < nf; ++i) {
+        uint32_t w;
+        memcpy(&w, &host[i], 4);
+        if (w & 0xffffu) return reject("bf16 array holds a value bf16 cannot represent");
+      }
+  }
+  if (host_checksum(host.data(), nf) != r->checksum) {
+    H->cnt.restores_rejected++;
+    return fail(SSM_E_SCHEMA, "deserialize: checksum mismatch (state does not match its receipt)");
+  }
+  hipStream_t s = as_stream(stream);
+  HIP_TRY(hipMemcpyAsync(H->slot_state(slot), host.data(), H->state_bytes(),
+                         hipMemcpyHostToDevice, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  adopt_receipt(H, slot, r);
   return SSM_OK;
 }
 

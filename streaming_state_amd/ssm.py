@@ -115,6 +115,9 @@ _SIGS = {
     "ssm_state_materialize": [_H, _I32, _V, _V],
     "ssm_state_checkpoint": [_H, _I32, _V, ctypes.POINTER(Receipt), _V],
     "ssm_state_restore": [_H, _I32, _V, ctypes.POINTER(Receipt), _V],
+    "ssm_blob_bytes": [ctypes.POINTER(LayerDesc)],
+    "ssm_state_serialize": [_H, _I32, _V, _SZ, ctypes.POINTER(_SZ), ctypes.POINTER(Receipt), _V],
+    "ssm_state_deserialize": [_H, _I32, _V, _SZ, ctypes.POINTER(Receipt), _V],
     "ssm_get_position": [_H, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_U64)],
     "ssm_get_log_state": [_H, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)],
     "ssm_get_counters": [_H, ctypes.POINTER(Counters)],
@@ -392,6 +395,24 @@ class StreamState:
                                       _dev_ptr(src, torch.float32,
                                                (self.H, self.P, self.N), "src"),
                                       ctypes.byref(r), _stream(stream)))
+
+    def blob_bytes(self):
+        return int(_lib.ssm_blob_bytes(ctypes.byref(self.desc)))
+
+    def serialize(self, slot, stream=None):
+        """The slot's state as a state blob (bytes) and its receipt."""
+        cap = self.blob_bytes()
+        buf = ctypes.create_string_buffer(cap)
+        n, r = _SZ(0), Receipt()
+        _check(_lib.ssm_state_serialize(self.handle, int(slot), buf, cap, ctypes.byref(n),
+                                        ctypes.byref(r), _stream(stream)))
+        return buf.raw[:n.value], r.as_dict()
+
+    def deserialize(self, slot, blob, receipt, stream=None):
+        blob = bytes(blob)
+        r = Receipt.from_dict(receipt)
+        _check(_lib.ssm_state_deserialize(self.handle, int(slot), blob, len(blob),
+                                          ctypes.byref(r), _stream(stream)))
 
     def position(self, slot):
         p, c = _I64(0), _U64(0)

@@ -52,3 +52,11 @@ def assert_close(gpu, ref, rtol, atol, what=""):
             f"{what}: {int(bad.sum())}/{bad.size} elements outside tolerance "
             f"(rtol={rtol}, atol={atol}); worst at {i}: gpu={gpu[i]!r} ref={ref[i]!r}")
     return float(err.max()) if err.size else 0.0
+
+
+def receipt_checksum(words):
+    """A receipt's checksum as the library header defines it: the sum over the
+    state's 32-bit words w_i of w_i * (2i + 1), modulo 2^64."""
+    w = np.frombuffer(np.ascontiguousarray(words, dtype=np.float32).tobytes(), dtype="<u4")
+    i = np.arange(w.size, dtype=np.uint64)
+    return int(np.sum(w.astype(np.uint64) * (2 * i + 1), dtype=np.uint64))

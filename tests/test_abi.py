@@ -8,7 +8,10 @@ an empty chunk, succeeds) before anything is enqueued.
 import ctypes
 import re
 
+import numpy as np
 import pytest
+
+from tests.gpu_helpers import receipt_checksum
 
 ssm = pytest.importorskip("streaming_state_amd.ssm",
                           reason="libssm_stream.so not built (python -m streaming_state_amd.build)")
@@ -173,3 +176,65 @@ def test_size_queries():
     # the log holds two halves of W entries of dt[H], x[H,P], B[G,N] per slot
     entry = (128 + 128 * 64 + 128) * 4
     assert lib.ssm_replay_log_bytes(ctypes.byref(d), 256, 16) >= 256 * 2 * 16 * entry
+
+
+def test_blob_size_and_serialize_argument_checks():
+    lib = ssm.lib()
+    d = _desc(H=4, P=8, N=16)
+    assert lib.ssm_blob_bytes(ctypes.byref(d)) == 28 + 4 * 8 * 16 * 4
+    assert lib.ssm_blob_bytes(ctypes.byref(_desc(N=6))) == 0
+    rc, h = _create(desc=d)
+    n, r = ctypes.c_size_t(0), ssm.Receipt()
+    buf = ctypes.create_string_buffer(64)
+    assert lib.ssm_state_serialize(h, 0, buf, 64, ctypes.byref(n), ctypes.byref(r),
+                                   None) == ssm.SSM_E_INVALID_ARG
+    assert "capacity" in _err()
+    assert lib.ssm_state_serialize(h, 9, buf, 64, ctypes.byref(n), ctypes.byref(r),
+                                   None) == ssm.SSM_E_INVALID_ARG
+    lib.ssm_destroy(h)
+
+
+def test_deserialize_rejects_before_any_device_work():
+    """Every rejection below happens on the host; the slot and counters show it."""
+    from oracle import blob
+    lib = ssm.lib()
+    d = _desc(H=4, P=8, N=16)
+    rc, h = _create(desc=d)
+    state = np.arange(4 * 8 * 16, dtype=np.float32).reshape(4, 8, 16) / 64
+    good_r = dict(stream_id=5, model_rev=77, code_rev=ssm.code_rev(), schema_version=3,
+                  state_dtype=0, H=4, P=8, N=16, G=1, position=10, chunk_seq=2,
+                  checksum=receipt_checksum(state))
+    conv = np.zeros((1, 8, 4), np.float32)
+    ok = blob.write([(0, state)])
+    off = state + np.float32(2.0 ** -20)  # not bf16 numbers
+    off_b = blob.write([(0, off)])
+    cases = [
+        ("receipt model revision", ok, dict(good_r, model_rev=1)),
+        ("checksum mismatch", ok, dict(good_r, checksum=1)),
+        ("not [H, P, N]", blob.write([(0, state.reshape(4, 16, 8))]), good_r),
+        ("not [H, P, N]", blob.write([(0, state.reshape(32, 16))]), good_r),
+        ("not [H, P, N]", blob.write([(0, np.stack([state, state]))]), good_r),
+        ("not [H, P, N]", blob.write([(0, state), (0, conv)]), good_r),
+        ("truncated", ok[:-4], good_r),
+        ("trailing bytes", ok + b"\0\0\0\0", good_r),
+        ("version", b"\x02\0\0\0" + ok[4:], good_r),
+        ("unknown dtype code", ok[:24] + b"\x05\0\0\0" + ok[28:], good_r),
+        ("bf16 cannot represent", off_b[:24] + b"\x02\0\0\0" + off_b[28:],
+         dict(good_r, checksum=receipt_checksum(off))),
+        ("shorter than its header", b"", good_r),
+    ]
+    for what, b, rd in cases:
+        r = ssm.Receipt.from_dict(rd)
+        assert lib.ssm_state_deserialize(h, 1, b, len(b), ctypes.byref(r),
+                                         None) == ssm.SSM_E_SCHEMA, what
+        assert what in _err(), (what, _err())
+    c = ssm.Counters()
+    lib.ssm_get_counters(h, ctypes.byref(c))
+    assert c.restores_rejected == len(cases) and c.restores == 0
+    pos, seq = ctypes.c_int64(-1), ctypes.c_uint64(9)
+    lib.ssm_get_position(h, 1, ctypes.byref(pos), ctypes.byref(seq))
+    assert pos.value == 0 and seq.value == 0
+    r = ssm.Receipt.from_dict(good_r)
+    assert lib.ssm_state_deserialize(h, 1, None, 0, ctypes.byref(r),
+                                     None) == ssm.SSM_E_INVALID_ARG
+    lib.ssm_destroy(h)
