@@ -48,15 +48,48 @@ DECODE_COUNTERS = {
 }
 
 
-def counter_traffic():
-    """Scaled HBM bytes per decode launch, or None if the kernel changed."""
+# The same for scan_ssd_kernel on the 65,536-token prefill (mean per dispatch
+# over 4 dispatches): MFMA busy cycles summed over all SIMDs, GPU-active
+# cycles summed over the 8 XCDs, bf16 MFMA operations (x512 = flops), and the
+# HBM counters with the copy calibration above.
+PREFILL_COUNTERS = {
+    "sources": ["ssm_ssd.hip", "ssm_device.h", "ssm_internal.h"],
+    "sha256": "829d66e195aa6b6c044a77a179e216c18a492967f06eec8ad0cdd1fd44fb5fce",
+    "mfma_busy_cycles": 420020224.0, "gui_active_cycles": 19989437.75, "xcds": 8, "simds": 1024,
+    "mfma_mops_bf16": 840040448.0,
+    "fetch_kib": 738667.48, "write_kib": 1085440.71,
+    "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2**25 + 2 * 2**22,
+}
+
+
+def _sources_match(c):
     import hashlib
-    c = DECODE_COUNTERS
     h = hashlib.sha256()
     for f in c["sources"]:
         with open(os.path.join(ROOT, "streaming_state_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest() != c["sha256"]:
+    return h.hexdigest() == c["sha256"]
+
+
+def prefill_counters():
+    """MFMA utilisation and scaled HBM bytes of one prefill launch from the
+    recorded counters, or None if the kernel changed since they were taken."""
+    c, d = PREFILL_COUNTERS, DECODE_COUNTERS
+    if not _sources_match(c):
+        return None
+    per_xcd = c["gui_active_cycles"] / c["xcds"]
+    kib = (c["fetch_kib"] * d["calib_true_kib"] / d["calib_fetch_kib"]
+           + c["write_kib"] * d["calib_true_kib"] / d["calib_write_kib"])
+    return {"mfma_busy_frac": round(c["mfma_busy_cycles"] / (per_xcd * c["simds"]), 4),
+            "mfma_flops_executed": c["mfma_mops_bf16"] * 512,
+            "traffic": round(kib * 1024),
+            "traffic_over_algorithmic": round(kib * 1024 / c["algorithmic_bytes"], 4)}
+
+
+def counter_traffic():
+    """Scaled HBM bytes per decode launch, or None if the kernel changed."""
+    c = DECODE_COUNTERS
+    if not _sources_match(c):
         return None, None
     kib = (c["fetch_kib"] * c["calib_true_kib"] / c["calib_fetch_kib"]
            + c["write_kib"] * c["calib_true_kib"] / c["calib_write_kib"])
@@ -279,7 +312,16 @@ def main():
         ms = np.array(t_pre.ms())
         comp["prefill"] = dict(ms_mean=float(ms.mean()), tokens_per_s=float(L4 / (ms.mean() * 1e-3)),
                                algorithmic_GFLOP=415.1)
-        comp["prefill"]["TFLOPs_algorithmic"] = 415.1e9 / (ms.mean() * 1e-3) / 1e12
+        tf = 415.1e9 / (ms.mean() * 1e-3) / 1e12
+        comp["prefill"]["TFLOPs_algorithmic"] = tf
+        pc = prefill_counters()
+        comp["prefill"]["roofline"] = {
+            "bound": "mfma", "kernel": "scan_ssd_kernel", "achieved": round(tf, 1),
+            "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4),
+            "mfma_busy_frac_counter": pc and pc["mfma_busy_frac"],
+            "mfma_flops_executed": pc and pc["mfma_flops_executed"],
+            "traffic": pc and pc["traffic"],
+            "traffic_over_algorithmic": pc and pc["traffic_over_algorithmic"]}
 
     # ------------------------------------------------------------- extras
     extras = {}
