@@ -12,6 +12,8 @@
 namespace ssm {
 
 static __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+static __device__ __forceinline__ float to_f(float v) { return v; }
+static __device__ __forceinline__ float to_f(bf16_t v) { return bf16_to_f(v); }
 
 // ===========================================================================
 // decode: h <- exp(dt A) h + dt x B^T ; y = h C + D x, one token per slot
@@ -184,40 +186,69 @@ struct LogIdx {
   }
 };
 
-// Pass 1: B_j . C_k for every combined entry j (committed log, then in-flight)
-// and in-flight token k, per (entry, group); these are shared by all heads of
-// a group.  Also appends the in-flight B rows to the live log half.
+// Staging loads of the verify kernels are issued in rounds of kStageU
+// values per thread: every load of a round is in flight before the first
+// LDS store of that round waits for it.
+constexpr int kStageU = 4;
+
+// Pass 1, per (batch entry, group): B_j . C_k for every combined entry j
+// (committed log, then in-flight) and in-flight token k; these are shared by
+// all heads of a group.  The rows are staged in LDS with one batch of loads
+// (row stride N/4 + 1 float4, so rows start on distinct 16-byte slots), and
+// the in-flight B rows are appended to the live log half on the way.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, ReplayMeta m,
                                                              LogLayout lay) {
+  extern __shared__ float4 bc_smem[];
   const Dims d = a.d;
   const int e = blockIdx.x / d.G, g = blockIdx.x % d.G;
   const int slot = m.slot[e];
   const int base = m.base_len[e];
   const int wh = (m.halves[e] >> 1) & 1;
-  const int J = base + a.n_in;
+  const int n_in = a.n_in, J = base + n_in;
+  const int q = d.N >> 2, qs = q + 1;
+  float4 *sB = bc_smem;                    // [J][qs]
+  float4 *sC = bc_smem + (size_t)a.W * qs;  // [n_in][qs]
   const LogIdx li{a.W};
   T *logB = (T *)((char *)a.log + lay.B_off);
   const T *inB = (const T *)a.B, *inC = (const T *)a.C;
-  // append in-flight B rows
-  for (int i = threadIdx.x; i < a.n_in * d.N; i += kThreads) {
-    const int k = i / d.N, n = i % d.N;
-    const size_t ek = (size_t)e * a.n_in + k;
-    logB[(li.ent(slot, wh, base + k) * d.G + g) * d.N + n] = inB[(ek * d.G + g) * d.N + n];
-  }
-  // dot products: one wave per (j, k) pair, lanes over n
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float *bc = a.bc + ((size_t)e * d.G + g) * a.W * kMaxInFlight;
-  for (int pr = wave; pr < J * a.n_in; pr += kThreads / 64) {
-    const int j = pr / a.n_in, k = pr % a.n_in;
-    const T *Bj = j < base ? logB + (li.ent(slot, wh, j) * d.G + g) * d.N
-                           : inB + (((size_t)e * a.n_in + (j - base)) * d.G + g) * d.N;
-    const T *Ck = inC + (((size_t)e * a.n_in + k) * d.G + g) * d.N;
-    float acc = 0.f;
-    for (int n = lane; n < d.N; n += 64) acc += Io<T>::ld(Bj + n) * Io<T>::ld(Ck + n);
+  const int total = (J + n_in) * q;
+  for (int i0 = 0; i0 < total; i0 += kStageU * kThreads) {
+    float4 v[kStageU];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) bc[j * kMaxInFlight + k] = acc;
+    for (int u = 0; u < kStageU; ++u) {
+      const int i = i0 + u * kThreads + (int)threadIdx.x;
+      if (i < total) {
+        const int row = i / q, cq = i - row * q;
+        const T *src = row < base ? logB + (li.ent(slot, wh, row) * d.G + g) * d.N
+                       : row < J  ? inB + (((size_t)e * n_in + (row - base)) * d.G + g) * d.N
+                                  : inC + (((size_t)e * n_in + (row - J)) * d.G + g) * d.N;
+        v[u] = Io<T>::ld4(src + 4 * cq);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int i = i0 + u * kThreads + (int)threadIdx.x;
+      if (i < total) {
+        const int row = i / q, cq = i - row * q;
+        if (row < J) {
+          sB[row * qs + cq] = v[u];
+          if (row >= base)
+            Io<T>::st4(logB + (li.ent(slot, wh, row) * d.G + g) * d.N + 4 * cq, v[u]);
+        } else {
+          sC[(row - J) * qs + cq] = v[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  float *bc = a.bc + ((size_t)e * d.G + g) * a.W * kMaxInFlight;
+  for (int p = threadIdx.x; p < J * n_in; p += kThreads) {
+    const int j = p / n_in, k = p - j * n_in;
+    const float4 *bj = sB + j * qs, *ck = sC + k * qs;
+    float acc = 0.f;
+    for (int t = 0; t < q; ++t) acc += dot4(bj[t], ck[t]);
+    bc[j * kMaxInFlight + k] = acc;
   }
 }
 
@@ -228,15 +259,72 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
 //   y_k = Lambda_m (ckpt . C_k) + sum_{j<=m} w_{j,m} x_j (B_j . C_k) + D x_k,
 // m = base + k, Lambda_m = exp(A sum_{i<=m} dt_i),
 // w_{j,m} = exp(A sum_{j<i<=m} dt_i) dt_j  (direct suffix sums, at most W terms).
-constexpr int kReplayR = 8;  // 32 KiB tiles: its per-workgroup setup (log staging, decay
-                             // weights) costs more than 16 KiB tiles gain
+// Everything the tile needs besides the checkpoint (log and in-flight x, the
+// fold's B rows, the in-flight C rows) is copied global -> LDS by
+// global_load_lds_dwordx4, issued together with the checkpoint's loads: no
+// registers hold it on the way, so the kernel keeps eight workgroups per CU,
+// and a workgroup waits on global memory once; every later phase touches only
+// LDS and registers.
+constexpr int kReplayR = 8;  // 64-row (32 KiB) tiles
+
+// LDS carve-up of the verify kernel (byte offsets; W window, n_in in-flight
+// tokens, rows = the tile's row count, es = io element size):
+//   V [W + n_in][N] io   fold B rows, then in-flight C rows
+//   x [W + n_in][rows] io combined entries' x, then the fold entries' x
+//   dt [W], fdt [W], coef [W][n_in] (staged B.C, then the weights),
+//   lam [n_in], fw [W], flam [1], dot [n_in][rows]   (fp32)
+struct ReplaySmem {
+  int V, x, dt, fdt, coef, lam, fw, flam, dot, total;
+  __host__ __device__ ReplaySmem(int W, int n_in, int N, int rows, int es) {
+    auto up16 = [](int b) { return (b + 15) & ~15; };
+    V = 0;
+    x = up16(V + (W + n_in) * N * es);
+    dt = up16(x + (W + n_in) * rows * es);
+    fdt = dt + 4 * W;
+    coef = fdt + 4 * W;
+    lam = coef + 4 * W * n_in;
+    fw = lam + 4 * n_in;
+    flam = fw + 4 * W;
+    dot = flam + 4;
+    total = dot + 4 * n_in * rows;
+  }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Copy n 16-byte chunks global -> LDS: chunk i lands at lds + 16 i, read from
+// src_of(i).  Each wave instruction fills 64 consecutive chunks (lane l
+// writes 16 bytes at the wave's LDS base + 16 l; inactive lanes write
+// nothing).  The copies complete asynchronously: wait on vmcnt before use.
+template <typename SrcOf>
+__device__ __forceinline__ void stage_lds(char *lds, int n, SrcOf src_of) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  for (int blk = wave; blk * 64 < n; blk += kThreads / 64) {
+    const int i = blk * 64 + lane;
+    if (i < n)
+      __builtin_amdgcn_global_load_lds(src_of(i), (lds_void_t *)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+template <typename T> __device__ __forceinline__ float4 lds_ld4(const T *p);
+template <> __device__ __forceinline__ float4 lds_ld4<float>(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+template <> __device__ __forceinline__ float4 lds_ld4<bf16_t>(const bf16_t *p) {
+  const uint2 r = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+}
 
 template <typename T, int R>
 __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMeta m,
                                                           LogLayout lay) {
-  extern __shared__ float smem[];
+  extern __shared__ float4 rp_smem4[];
+  char *sb = reinterpret_cast<char *>(rp_smem4);
   const TileR<R> tl;
   constexpr int kRows = 8 * R;  // state rows of this workgroup's tile
+  constexpr int E = 16 / (int)sizeof(T);  // io elements per 16-byte chunk
   const Dims d = a.d;
   const int W = a.W, n_in = a.n_in;
   const int pt_n = (d.P + kRows - 1) / kRows;
@@ -252,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   const int J = base + n_in;
   const int g = h / (d.H / d.G);
   const int prow0 = pt * kRows;
+  const int rv = min(kRows, d.P - prow0);  // rows of this tile inside the head
   const bool colok = 4 * tl.c < d.N;
   const size_t PN = (size_t)d.P * d.N;
   const float Ah = a.A[h], Dh = a.D[h];
@@ -260,65 +349,82 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   T *logx = (T *)((char *)a.log + lay.x_off);
   const T *logB = (const T *)((const char *)a.log + lay.B_off);
   const T *inx = (const T *)a.x, *indt = (const T *)a.dt, *inC = (const T *)a.C;
+  const ReplaySmem L(W, n_in, d.N, rv, (int)sizeof(T));
+  T *s_V = (T *)(sb + L.V);  // [F + n_in][N]
+  T *s_x = (T *)(sb + L.x);  // [J + F][rv]
+  float *s_dt = (float *)(sb + L.dt), *s_fdt = (float *)(sb + L.fdt);
+  float *s_coef = (float *)(sb + L.coef), *s_lam = (float *)(sb + L.lam);
+  float *s_fw = (float *)(sb + L.fw), *s_flam = (float *)(sb + L.flam);
+  float *s_dot = (float *)(sb + L.dot);
 
-  // checkpoint tile first
+  // start of the tile's rows of combined entry j (j < J) or fold entry j - J
+  auto x_src = [&](int j) -> const T * {
+    return j >= J     ? logx + (li.ent(slot, rh, j - J) * d.H + h) * d.P + prow0
+           : j < base ? logx + (li.ent(slot, wh, j) * d.H + h) * d.P + prow0
+                      : inx + (((size_t)e * n_in + (j - base)) * d.H + h) * d.P + prow0;
+  };
+  // fold B row r (r < F), then in-flight C row r - F
+  auto v_src = [&](int r) -> const T * {
+    return r < F ? logB + (li.ent(slot, rh, r) * d.G + g) * d.N
+                 : inC + (((size_t)e * n_in + (r - F)) * d.G + g) * d.N;
+  };
+  const bool whole_chunks = (d.P * (int)sizeof(T)) % 16 == 0 && (d.N * (int)sizeof(T)) % 16 == 0 &&
+                           (((uintptr_t)a.x | (uintptr_t)a.C) & 15) == 0;
+  if (whole_chunks) {
+    const int cx = rv / E, cv = d.N / E;
+    stage_lds(sb + L.x, (J + F) * cx, [&](int i) {
+      const int j = i / cx;
+      return (const void *)(x_src(j) + (i - j * cx) * E);
+    });
+    stage_lds(sb + L.V, (F + n_in) * cv, [&](int i) {
+      const int r = i / cv;
+      return (const void *)(v_src(r) + (i - r * cv) * E);
+    });
+  } else {  // rows not made of aligned 16-byte chunks: element copies
+    for (int i = threadIdx.x; i < (J + F) * rv; i += kThreads) {
+      const int j = i / rv;
+      s_x[i] = x_src(j)[i - j * rv];
+    }
+    for (int i = threadIdx.x; i < (F + n_in) * d.N; i += kThreads) {
+      const int r = i / d.N;
+      s_V[i] = v_src(r)[i - r * d.N];
+    }
+  }
+
+  // checkpoint tile
   float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * d.N + 4 * tl.c;
   float4 hv[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const bool ok = colok && (prow0 + tl.row(i) < d.P);
+    const bool ok = colok && (tl.row(i) < rv);
     hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * d.N) : zero4();
   }
 
-  // LDS carve-up (sizes from the host): fold x [W][64], fold dt/w [W],
-  // combined dt [W], combined x [W][64], coef [W][kMaxInFlight],
-  // lambda [kMaxInFlight], dot [kMaxInFlight][64], fold lambda [1]
-  float *s_fx = smem;
-  float *s_fdt = s_fx + W * kRows;
-  float *s_fw = s_fdt + W;
-  float *s_dt = s_fw + W;
-  float *s_x = s_dt + W;
-  float *s_coef = s_x + W * kRows;
-  float *s_lam = s_coef + W * kMaxInFlight;
-  float *s_dot = s_lam + kMaxInFlight;
-  float *s_flam = s_dot + kMaxInFlight * kRows;
-
-  // stage fold entries (read half), combined entries, and append in-flight x/dt
-  for (int i = threadIdx.x; i < F * kRows; i += kThreads) {
-    const int j = i / kRows, r = i % kRows;
-    s_fx[i] = prow0 + r < d.P
-                  ? Io<T>::ld(logx + (li.ent(slot, rh, j) * d.H + h) * d.P + prow0 + r)
-                  : 0.f;
-  }
-  for (int j = threadIdx.x; j < F; j += kThreads)
-    s_fdt[j] = Io<T>::ld(logdt + li.ent(slot, rh, j) * d.H + h);
-  for (int i = threadIdx.x; i < J * kRows; i += kThreads) {
-    const int j = i / kRows, r = i % kRows;
-    float v = 0.f;
-    if (prow0 + r < d.P) {
-      if (j < base) {
-        v = Io<T>::ld(logx + (li.ent(slot, wh, j) * d.H + h) * d.P + prow0 + r);
-      } else {
-        const T *src = inx + (((size_t)e * n_in + (j - base)) * d.H + h) * d.P + prow0 + r;
-        const T raw = *src;
-        v = Io<T>::ld(src);
-        logx[(li.ent(slot, wh, j) * d.H + h) * d.P + prow0 + r] = raw;
-      }
-    }
-    s_x[i] = v;
-  }
-  for (int j = threadIdx.x; j < J; j += kThreads) {
-    float v;
-    if (j < base) {
-      v = Io<T>::ld(logdt + li.ent(slot, wh, j) * d.H + h);
+  // scalars: combined dt, fold dt, B.C products
+  const float *bc = a.bc + ((size_t)e * d.G + g) * W * kMaxInFlight;
+  const int nS = J + F + J * n_in;
+  for (int i = threadIdx.x; i < nS; i += kThreads) {
+    if (i < J) {
+      s_dt[i] = to_f(i < base ? logdt[li.ent(slot, wh, i) * d.H + h]
+                              : indt[((size_t)e * n_in + (i - base)) * d.H + h]);
+    } else if (i < J + F) {
+      s_fdt[i - J] = to_f(logdt[li.ent(slot, rh, i - J) * d.H + h]);
     } else {
-      const T *src = indt + ((size_t)e * n_in + (j - base)) * d.H + h;
-      v = Io<T>::ld(src);
-      if (pt == 0) logdt[li.ent(slot, wh, j) * d.H + h] = *src;
+      const int p = i - J - F, j = p / n_in, k = p - j * n_in;
+      s_coef[p] = bc[j * kMaxInFlight + k];
     }
-    s_dt[j] = v;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the LDS copies above have landed
   __syncthreads();
+
+  // append the in-flight x and dt to the live log half
+  for (int i = threadIdx.x; i < n_in * rv; i += kThreads) {
+    const int k = i / rv, r = i - k * rv;
+    logx[(li.ent(slot, wh, base + k) * d.H + h) * d.P + prow0 + r] = s_x[(base + k) * rv + r];
+  }
+  if (pt == 0)
+    for (int k = threadIdx.x; k < n_in; k += kThreads)
+      Io<T>::st(logdt + li.ent(slot, wh, base + k) * d.H + h, s_dt[base + k]);
 
   // scalar weights
   for (int j = threadIdx.x; j < F; j += kThreads) {
@@ -326,21 +432,20 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
     for (int i = j + 1; i < F; ++i) suf += s_fdt[i];
     s_fw[j] = expf(Ah * suf) * s_fdt[j];
   }
-  if (threadIdx.x == kThreads - 1) {
+  if (F > 0 && threadIdx.x == kThreads - 1) {
     float tot = 0.f;
     for (int i = 0; i < F; ++i) tot += s_fdt[i];
     s_flam[0] = expf(Ah * tot);
   }
-  const float *bc = a.bc + ((size_t)e * d.G + g) * W * kMaxInFlight;
   for (int t = threadIdx.x; t < J * n_in; t += kThreads) {
     const int j = t / n_in, k = t % n_in, mm = base + k;
     float cf = 0.f;
     if (j <= mm) {
       float suf = 0.f;
       for (int i = j + 1; i <= mm; ++i) suf += s_dt[i];
-      cf = expf(Ah * suf) * s_dt[j] * bc[j * kMaxInFlight + k];
+      cf = expf(Ah * suf) * s_dt[j] * s_coef[t];
     }
-    s_coef[j * kMaxInFlight + k] = cf;
+    s_coef[t] = cf;
   }
   for (int k = threadIdx.x; k < n_in; k += kThreads) {
     float tot = 0.f;
@@ -355,68 +460,89 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
 #pragma unroll
     for (int i = 0; i < R; ++i)
       hv[i] = make_float4(lam * hv[i].x, lam * hv[i].y, lam * hv[i].z, lam * hv[i].w);
+    const T *fx = s_x + J * rv;
     for (int j = 0; j < F; ++j) {
-      float4 Bv = zero4();
-      if (colok) Bv = Io<T>::ld4(logB + (li.ent(slot, rh, j) * d.G + g) * d.N + 4 * tl.c);
+      const float4 Bv = colok ? lds_ld4(s_V + j * d.N + 4 * tl.c) : zero4();
       const float w = s_fw[j];
 #pragma unroll
-      for (int i = 0; i < R; ++i) hv[i] = fma4(1.f, hv[i], w * s_fx[j * kRows + tl.row(i)], Bv);
+      for (int i = 0; i < R; ++i) {
+        const float xv = tl.row(i) < rv ? to_f(fx[j * rv + tl.row(i)]) : 0.f;
+        hv[i] = fma4(1.f, hv[i], w * xv, Bv);
+      }
     }
 #pragma unroll
     for (int i = 0; i < R; ++i)
-      if (colok && prow0 + tl.row(i) < d.P) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
+      if (colok && tl.row(i) < rv) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
   }
 
   // ckpt . C_k for every in-flight token
+  const T *s_C = s_V + F * d.N;
   for (int k = 0; k < n_in; ++k) {
-    float4 Cv = zero4();
-    if (colok) Cv = Io<T>::ld4(inC + (((size_t)e * n_in + k) * d.G + g) * d.N + 4 * tl.c);
+    const float4 Cv = colok ? lds_ld4(s_C + k * d.N + 4 * tl.c) : zero4();
     float part[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) part[i] = dot4(hv[i], Cv);
     const float v = reduce_rows<R>(part, tl.lane);
-    if (tl.reduced_writer()) s_dot[k * kRows + tl.reduced_row()] = v;
+    if (tl.reduced_writer() && tl.reduced_row() < rv) s_dot[k * rv + tl.reduced_row()] = v;
   }
   __syncthreads();
 
   // outputs
-  for (int i = threadIdx.x; i < n_in * kRows; i += kThreads) {
-    const int k = i / kRows, r = i % kRows;
-    if (prow0 + r >= d.P) continue;
+  for (int i = threadIdx.x; i < n_in * rv; i += kThreads) {
+    const int k = i / rv, r = i - k * rv;
     const int mm = base + k;
-    float acc = s_lam[k] * s_dot[k * kRows + r];
-    for (int j = 0; j <= mm; ++j) acc += s_coef[j * kMaxInFlight + k] * s_x[j * kRows + r];
-    acc += Dh * s_x[mm * kRows + r];
+    float acc = s_lam[k] * s_dot[k * rv + r];
+    for (int j = 0; j <= mm; ++j) acc += s_coef[j * n_in + k] * to_f(s_x[j * rv + r]);
+    acc += Dh * to_f(s_x[mm * rv + r]);
     Io<T>::st((T *)a.y + (((size_t)e * n_in + k) * d.H + h) * d.P + prow0 + r, acc);
   }
 }
 
-static size_t replay_smem_bytes(int W) {
-  constexpr int kRows = 8 * kReplayR;
-  return sizeof(float) *
-         ((size_t)W * kRows + W + W + W + (size_t)W * kRows + (size_t)W * kMaxInFlight +
-          kMaxInFlight + (size_t)kMaxInFlight * kRows + 1);
+static size_t replay_smem_bytes(int io, int W, int n_in, int N) {
+  return (size_t)ReplaySmem(W, n_in, N, 8 * kReplayR, io == kBF16 ? 2 : 4).total;
+}
+
+static size_t replay_bc_smem_bytes(int W, int n_in, int N) {
+  return sizeof(float4) * (size_t)(W + n_in) * (N / 4 + 1);
+}
+
+// Dynamic LDS above 64 KiB needs the kernel's limit raised once.
+template <typename K> static hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const LogLayout &lay,
                          hipStream_t s) {
   if (a.n_in > 0) {
     dim3 g1(a.n * a.d.G), b1(kThreads);
-    if (io == kBF16)
-      hipLaunchKernelGGL(replay_bc_kernel<bf16_t>, g1, b1, 0, s, a, m, lay);
-    else
-      hipLaunchKernelGGL(replay_bc_kernel<float>, g1, b1, 0, s, a, m, lay);
-    hipError_t err = hipGetLastError();
+    const size_t sm1 = replay_bc_smem_bytes(a.W, a.n_in, a.d.N);
+    hipError_t err;
+    if (io == kBF16) {
+      err = allow_lds(replay_bc_kernel<bf16_t>, sm1);
+      if (err == hipSuccess) hipLaunchKernelGGL(replay_bc_kernel<bf16_t>, g1, b1, sm1, s, a, m, lay);
+    } else {
+      err = allow_lds(replay_bc_kernel<float>, sm1);
+      if (err == hipSuccess) hipLaunchKernelGGL(replay_bc_kernel<float>, g1, b1, sm1, s, a, m, lay);
+    }
+    if (err == hipSuccess) err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const int pt_n = (a.d.P + 8 * kReplayR - 1) / (8 * kReplayR);
   dim3 grid(a.n * a.d.H * pt_n), block(kThreads);
-  const size_t sm = replay_smem_bytes(a.W);
-  if (io == kBF16)
-    hipLaunchKernelGGL((replay_kernel<bf16_t, kReplayR>), grid, block, sm, s, a, m, lay);
-  else
-    hipLaunchKernelGGL((replay_kernel<float, kReplayR>), grid, block, sm, s, a, m, lay);
-  return hipGetLastError();
+  const size_t sm = replay_smem_bytes(io, a.W, a.n_in, a.d.N);
+  hipError_t err;
+  if (io == kBF16) {
+    err = allow_lds(replay_kernel<bf16_t, kReplayR>, sm);
+    if (err == hipSuccess)
+      hipLaunchKernelGGL((replay_kernel<bf16_t, kReplayR>), grid, block, sm, s, a, m, lay);
+  } else {
+    err = allow_lds(replay_kernel<float, kReplayR>, sm);
+    if (err == hipSuccess)
+      hipLaunchKernelGGL((replay_kernel<float, kReplayR>), grid, block, sm, s, a, m, lay);
+  }
+  return err == hipSuccess ? hipGetLastError() : err;
 }
 
 // ===========================================================================
