@@ -60,8 +60,10 @@ template <> struct Io<bf16_t> {
 // fp32 state.  Lane l of wave w holds float4 column c = l & 31 (state entries
 // n = 4c..4c+3) of rows r_i = 8*i + 2*w + (l >> 5), i = 0..R-1.  One wave-wide
 // load instruction therefore covers two adjacent rows (2 * 512 B contiguous
-// at N = 128).
-template <int R>
+// at N = 128).  With kContig the R rows of a lane are consecutive instead,
+// r_i = R*(2*w + (l >> 5)) + i, so per-row values staged in LDS are read as
+// whole vectors; each load instruction then covers two separate full rows.
+template <int R, bool kContig = false>
 struct TileR {
   static constexpr int kRowsPerTile = 8 * R;
   int lane, wave, c, rsub;
@@ -71,7 +73,9 @@ struct TileR {
     c = lane & 31;
     rsub = lane >> 5;
   }
-  __device__ __forceinline__ int row(int i) const { return 8 * i + 2 * wave + rsub; }
+  __device__ __forceinline__ int row(int i) const {
+    return kContig ? R * (2 * wave + rsub) + i : 8 * i + 2 * wave + rsub;
+  }
   // Row (within the tile) whose total this lane holds after reduce_rows<R>().
   __device__ __forceinline__ int reduced_row() const {
     const int b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
@@ -145,6 +149,60 @@ template <> __device__ __forceinline__ float reduce_rows<4>(const float v[4], in
   return reduce4(v, lane);
 }
 
+// The same row totals with VALU lane moves only (no LDS round trips): the
+// 32-lane halving step pairs lane j of a 16-lane row with lane j of the next
+// row (v_permlane16_swap), the 8- and 4-lane steps pair mirrored lanes
+// (DPP row_mirror, row_half_mirror), and the last two sums run inside quads.
+// A lane keeps the same half as in the xor form, so reduced_row() and
+// reduced_writer() hold for it too; only the association of the sum differs.
+template <int kCtrl> __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E;  // quad_perm [1,0,3,2], [2,3,0,1]
+// lanes of even rows keep lo, of odd rows hi; each gets its half's total over the row pair
+__device__ __forceinline__ float halve_rows(float lo, float hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// bit set: keep hi, else lo; the partner is the mirrored lane (opposite bit)
+template <int kCtrl> __device__ __forceinline__ float halve_mirror(float lo, float hi, int bit) {
+  return (bit ? hi : lo) + dpp_f<kCtrl>(bit ? lo : hi);
+}
+template <int R> __device__ __forceinline__ float row_totals(const float v[R], int lane);
+template <> __device__ __forceinline__ float row_totals<8>(const float v[8], int lane) {
+  const int b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+  float s4[4], s2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4[i] = halve_rows(v[i], v[i + 4]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) s2[i] = halve_mirror<kDppRowMirror>(s4[i], s4[i + 2], b3);
+  float s = halve_mirror<kDppRowHalfMirror>(s2[0], s2[1], b2);
+  s += dpp_f<kDppQuadXor2>(s);
+  s += dpp_f<kDppQuadXor1>(s);
+  return s;
+}
+template <> __device__ __forceinline__ float row_totals<4>(const float v[4], int lane) {
+  const int b3 = (lane >> 3) & 1;
+  float s2[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) s2[i] = halve_rows(v[i], v[i + 2]);
+  float s = halve_mirror<kDppRowMirror>(s2[0], s2[1], b3);
+  s += dpp_f<kDppRowHalfMirror>(s);
+  s += dpp_f<kDppQuadXor2>(s);
+  s += dpp_f<kDppQuadXor1>(s);
+  return s;
+}
+template <> __device__ __forceinline__ float row_totals<2>(const float v[2], int lane) {
+  float s = halve_rows(v[0], v[1]);
+  s += dpp_f<kDppRowMirror>(s);
+  s += dpp_f<kDppRowHalfMirror>(s);
+  s += dpp_f<kDppQuadXor2>(s);
+  s += dpp_f<kDppQuadXor1>(s);
+  return s;
+}
+
 // Sum over the 32 lanes of a row group with DPP lane moves (no LDS round
 // trip; the latency-critical form for the sequential scan).  Rotations by 1,
 // 2, 4 and 8 inside each 16-lane row leave every lane with its row's sum;
@@ -162,6 +220,19 @@ __device__ __forceinline__ float sum32_dpp(float v) {
   return v;
 }
 #undef SSM_DPP_ADD
+
+// Division of an index i < 2^16 by a block-uniform divisor 1 <= d < 2^16:
+// the high word of i * ceil(2^32 / d) is floor(i / d) in that range (the
+// rounding error of the multiplier, below d / 2^32 per unit of i, cannot
+// reach the next integer).  d = 1 is passed through (its multiplier would be 2^32).
+struct FastDiv {
+  uint32_t d, m;
+  __device__ __forceinline__ explicit FastDiv(int dv)
+      : d((uint32_t)dv), m(dv > 1 ? 0xffffffffu / (uint32_t)dv + 1u : 0u) {}
+  __device__ __forceinline__ int div(int i) const {
+    return d > 1 ? (int)__umulhi((uint32_t)i, m) : i;
+  }
+};
 
 // Streaming (nontemporal) 128-bit state accesses: the state is touched once
 // per step and the working set is far larger than the caches.

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads *TW) void decode_kernel(DecodeArgs a, Deco
     if (rowok && colok) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
     part[i] = dot4(hv[i], Cv);
   }
-  const float yv = reduce_rows<R>(part, tl.lane);
+  const float yv = row_totals<R>(part, tl.lane);
   const int r = tl.reduced_row();
   if (tl.reduced_writer() && prow0 + r < d.P)
     Io<T>::st((T *)a.y + ((size_t)e * d.H + h) * d.P + prow0 + r, yv + Dh * Io<T>::ld(x + r));
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a, CopyMeta m) 
       if (rowok && colok) nt_store4(out + (size_t)tl.row(i) * d.N, hv[i]);
       part[i] = dot4(hv[i], Cv);
     }
-    const float yv = reduce_rows<R>(part, tl.lane);
+    const float yv = row_totals<R>(part, tl.lane);
     const int r = tl.reduced_row();
     if (tl.reduced_writer() && prow0 + r < d.P)
       Io<T>::st((T *)a.y + (ek * d.H + h) * d.P + prow0 + r, yv + Dh * Io<T>::ld(x + r));
@@ -317,12 +317,39 @@ template <> __device__ __forceinline__ float4 lds_ld4<bf16_t>(const bf16_t *p) {
                      __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
 }
 
-template <typename T, int R>
-__global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMeta m,
+// R consecutive io values from LDS (16-byte aligned) as floats.
+template <typename T, int R> __device__ __forceinline__ void lds_ld_rows(const T *p, float *v) {
+  static_assert((R * sizeof(T)) % 16 == 0, "whole 16-byte reads");
+#pragma unroll
+  for (int q = 0; q < (int)(R * sizeof(T)) / 16; ++q) {
+    const uint4 u = reinterpret_cast<const uint4 *>(p)[q];
+    if (sizeof(T) == 4) {
+      v[4 * q + 0] = __uint_as_float(u.x);
+      v[4 * q + 1] = __uint_as_float(u.y);
+      v[4 * q + 2] = __uint_as_float(u.z);
+      v[4 * q + 3] = __uint_as_float(u.w);
+    } else {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[8 * q + 2 * t] = __uint_as_float(w[t] << 16);
+        v[8 * q + 2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// Eight waves per SIMD (<= 64 VGPRs): eight workgroups, 256 KiB of checkpoint
+// loads in flight per CU.  kFull: every tile has 64 rows inside the head and
+// N = 128, so every lane owns rows and columns and the fold and the dot
+// products need no per-lane predicates (a separate instantiation keeps the
+// register budget of each).
+template <typename T, int R, bool kFull>
+__global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, ReplayMeta m,
                                                           LogLayout lay) {
   extern __shared__ float4 rp_smem4[];
   char *sb = reinterpret_cast<char *>(rp_smem4);
-  const TileR<R> tl;
+  const TileR<R, true> tl;
   constexpr int kRows = 8 * R;  // state rows of this workgroup's tile
   constexpr int E = 16 / (int)sizeof(T);  // io elements per 16-byte chunk
   const Dims d = a.d;
@@ -341,6 +368,11 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   const int g = h / (d.H / d.G);
   const int prow0 = pt * kRows;
   const int rv = min(kRows, d.P - prow0);  // rows of this tile inside the head
+  const bool whole_chunks = (d.P * (int)sizeof(T)) % 16 == 0 && (d.N * (int)sizeof(T)) % 16 == 0 &&
+                            (((uintptr_t)a.x | (uintptr_t)a.C) & 15) == 0;
+  // LDS stride of an entry's x rows: rv for whole chunks (the copies are
+  // contiguous), else rounded up so that every 8-row group starts 16-byte aligned
+  const int xs = whole_chunks ? rv : (rv + 7) & ~7;
   const bool colok = 4 * tl.c < d.N;
   const size_t PN = (size_t)d.P * d.N;
   const float Ah = a.A[h], Dh = a.D[h];
@@ -351,43 +383,47 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   const T *inx = (const T *)a.x, *indt = (const T *)a.dt, *inC = (const T *)a.C;
   const ReplaySmem L(W, n_in, d.N, rv, (int)sizeof(T));
   T *s_V = (T *)(sb + L.V);  // [F + n_in][N]
-  T *s_x = (T *)(sb + L.x);  // [J + F][rv]
+  T *s_x = (T *)(sb + L.x);  // [J + F][xs]
   float *s_dt = (float *)(sb + L.dt), *s_fdt = (float *)(sb + L.fdt);
   float *s_coef = (float *)(sb + L.coef), *s_lam = (float *)(sb + L.lam);
   float *s_fw = (float *)(sb + L.fw), *s_flam = (float *)(sb + L.flam);
   float *s_dot = (float *)(sb + L.dot);
 
-  // start of the tile's rows of combined entry j (j < J) or fold entry j - J
-  auto x_src = [&](int j) -> const T * {
-    return j >= J     ? logx + (li.ent(slot, rh, j - J) * d.H + h) * d.P + prow0
-           : j < base ? logx + (li.ent(slot, wh, j) * d.H + h) * d.P + prow0
-                      : inx + (((size_t)e * n_in + (j - base)) * d.H + h) * d.P + prow0;
-  };
-  // fold B row r (r < F), then in-flight C row r - F
-  auto v_src = [&](int r) -> const T * {
-    return r < F ? logB + (li.ent(slot, rh, r) * d.G + g) * d.N
-                 : inC + (((size_t)e * n_in + (r - F)) * d.G + g) * d.N;
-  };
-  const bool whole_chunks = (d.P * (int)sizeof(T)) % 16 == 0 && (d.N * (int)sizeof(T)) % 16 == 0 &&
-                           (((uintptr_t)a.x | (uintptr_t)a.C) & 15) == 0;
+  // Five row sources, each a run of rows at a fixed stride: the committed
+  // and the in-flight x, the fold entries' x, the fold B rows and the
+  // in-flight C rows.  Consecutive log entries of a slot and half are
+  // consecutive in the log, so every run is (first row, stride, count).
+  const size_t xstride = (size_t)d.H * d.P, vstride = (size_t)d.G * d.N;
+  const T *x_com = logx + (li.ent(slot, wh, 0) * d.H + h) * d.P + prow0;
+  const T *x_new = inx + ((size_t)e * n_in * d.H + h) * d.P + prow0;
+  const T *x_fold = logx + (li.ent(slot, rh, 0) * d.H + h) * d.P + prow0;
+  const T *b_fold = logB + li.ent(slot, rh, 0) * vstride + (size_t)g * d.N;
+  const T *c_new = inC + (size_t)e * n_in * vstride + (size_t)g * d.N;
   if (whole_chunks) {
     const int cx = rv / E, cv = d.N / E;
-    stage_lds(sb + L.x, (J + F) * cx, [&](int i) {
-      const int j = i / cx;
-      return (const void *)(x_src(j) + (i - j * cx) * E);
-    });
-    stage_lds(sb + L.V, (F + n_in) * cv, [&](int i) {
-      const int r = i / cv;
-      return (const void *)(v_src(r) + (i - r * cv) * E);
-    });
+    const FastDiv fx(cx), fv(cv);
+    auto run = [&](char *lds, const T *src, size_t stride, int rows, int chunks, FastDiv f) {
+      stage_lds(lds, rows * chunks, [&](int i) {
+        const int j = f.div(i);
+        return (const void *)(src + j * stride + (i - j * chunks) * E);
+      });
+    };
+    run(sb + L.x, x_com, xstride, base, cx, fx);
+    run(sb + L.x + base * xs * (int)sizeof(T), x_new, xstride, n_in, cx, fx);
+    run(sb + L.x + J * xs * (int)sizeof(T), x_fold, xstride, F, cx, fx);
+    run(sb + L.V, b_fold, vstride, F, cv, fv);
+    run(sb + L.V + F * d.N * (int)sizeof(T), c_new, vstride, n_in, cv, fv);
   } else {  // rows not made of aligned 16-byte chunks: element copies
+    const FastDiv frv(rv), fn(d.N);
     for (int i = threadIdx.x; i < (J + F) * rv; i += kThreads) {
-      const int j = i / rv;
-      s_x[i] = x_src(j)[i - j * rv];
+      const int j = frv.div(i), r = i - j * rv;
+      const T *src = j >= J ? x_fold + (j - J) * xstride
+                     : j < base ? x_com + j * xstride : x_new + (j - base) * xstride;
+      s_x[j * xs + r] = src[r];
     }
     for (int i = threadIdx.x; i < (F + n_in) * d.N; i += kThreads) {
-      const int r = i / d.N;
-      s_V[i] = v_src(r)[i - r * d.N];
+      const int r = fn.div(i);
+      s_V[i] = (r < F ? b_fold + r * vstride : c_new + (r - F) * vstride)[i - r * d.N];
     }
   }
 
@@ -403,14 +439,17 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   // scalars: combined dt, fold dt, B.C products
   const float *bc = a.bc + ((size_t)e * d.G + g) * W * kMaxInFlight;
   const int nS = J + F + J * n_in;
+  const FastDiv fnin(n_in);
+  const T *dt_com = logdt + li.ent(slot, wh, 0) * d.H + h;
+  const T *dt_new = indt + (size_t)e * n_in * d.H + h;
+  const T *dt_fold = logdt + li.ent(slot, rh, 0) * d.H + h;
   for (int i = threadIdx.x; i < nS; i += kThreads) {
     if (i < J) {
-      s_dt[i] = to_f(i < base ? logdt[li.ent(slot, wh, i) * d.H + h]
-                              : indt[((size_t)e * n_in + (i - base)) * d.H + h]);
+      s_dt[i] = to_f(i < base ? dt_com[(size_t)i * d.H] : dt_new[(size_t)(i - base) * d.H]);
     } else if (i < J + F) {
-      s_fdt[i - J] = to_f(logdt[li.ent(slot, rh, i - J) * d.H + h]);
+      s_fdt[i - J] = to_f(dt_fold[(size_t)(i - J) * d.H]);
     } else {
-      const int p = i - J - F, j = p / n_in, k = p - j * n_in;
+      const int p = i - J - F, j = fnin.div(p), k = p - j * n_in;
       s_coef[p] = bc[j * kMaxInFlight + k];
     }
   }
@@ -418,9 +457,11 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   __syncthreads();
 
   // append the in-flight x and dt to the live log half
+  const FastDiv frows(rv);
+  T *x_app = logx + (li.ent(slot, wh, base) * d.H + h) * d.P + prow0;
   for (int i = threadIdx.x; i < n_in * rv; i += kThreads) {
-    const int k = i / rv, r = i - k * rv;
-    logx[(li.ent(slot, wh, base + k) * d.H + h) * d.P + prow0 + r] = s_x[(base + k) * rv + r];
+    const int k = frows.div(i), r = i - k * rv;
+    x_app[k * xstride + r] = s_x[(base + k) * xs + r];
   }
   if (pt == 0)
     for (int k = threadIdx.x; k < n_in; k += kThreads)
@@ -438,12 +479,13 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
     s_flam[0] = expf(Ah * tot);
   }
   for (int t = threadIdx.x; t < J * n_in; t += kThreads) {
-    const int j = t / n_in, k = t % n_in, mm = base + k;
+    const int j = fnin.div(t), k = t - j * n_in, mm = base + k;
     float cf = 0.f;
     if (j <= mm) {
       float suf = 0.f;
       for (int i = j + 1; i <= mm; ++i) suf += s_dt[i];
       cf = expf(Ah * suf) * s_dt[j] * s_coef[t];
+      if (j == mm) cf += Dh;  // the skip term D x_m rides on the newest entry
     }
     s_coef[t] = cf;
   }
@@ -454,47 +496,55 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a, ReplayMe
   }
   __syncthreads();
 
-  // fold the full log into the checkpoint and write it back
-  if (F > 0) {
-    const float lam = s_flam[0];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-      hv[i] = make_float4(lam * hv[i].x, lam * hv[i].y, lam * hv[i].z, lam * hv[i].w);
-    const T *fx = s_x + J * rv;
-    for (int j = 0; j < F; ++j) {
-      const float4 Bv = colok ? lds_ld4(s_V + j * d.N + 4 * tl.c) : zero4();
-      const float w = s_fw[j];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const float xv = tl.row(i) < rv ? to_f(fx[j * rv + tl.row(i)]) : 0.f;
-        hv[i] = fma4(1.f, hv[i], w * xv, Bv);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-      if (colok && tl.row(i) < rv) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
-  }
-
-  // ckpt . C_k for every in-flight token
+  // fold, then ckpt . C_k for every in-flight token
   const T *s_C = s_V + F * d.N;
-  for (int k = 0; k < n_in; ++k) {
-    const float4 Cv = colok ? lds_ld4(s_C + k * d.N + 4 * tl.c) : zero4();
-    float part[R];
+  {
+    const bool ck = kFull || colok;
+    if (F > 0) {
+      const float lam = s_flam[0];
 #pragma unroll
-    for (int i = 0; i < R; ++i) part[i] = dot4(hv[i], Cv);
-    const float v = reduce_rows<R>(part, tl.lane);
-    if (tl.reduced_writer() && tl.reduced_row() < rv) s_dot[k * rv + tl.reduced_row()] = v;
+      for (int i = 0; i < R; ++i)
+        hv[i] = make_float4(lam * hv[i].x, lam * hv[i].y, lam * hv[i].z, lam * hv[i].w);
+      const T *fx = s_x + J * xs + tl.row(0);  // this lane's R consecutive rows
+#pragma unroll 1
+      for (int j = 0; j < F; ++j) {
+        const float4 Bv = ck ? lds_ld4(s_V + j * d.N + 4 * tl.c) : zero4();
+        const float w = s_fw[j];
+        float xv[R];
+        lds_ld_rows<T, R>(fx + j * xs, xv);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          hv[i] = fma4(1.f, hv[i], (kFull || tl.row(i) < rv) ? w * xv[i] : 0.f, Bv);
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        if (ck && (kFull || tl.row(i) < rv)) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
+    }
+    for (int k = 0; k < n_in; ++k) {
+      const float4 Cv = ck ? lds_ld4(s_C + k * d.N + 4 * tl.c) : zero4();
+      float part[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) part[i] = dot4(hv[i], Cv);
+      const float v = row_totals<R>(part, tl.lane);
+      if (tl.reduced_writer() && (kFull || tl.reduced_row() < rv))
+        s_dot[k * rv + tl.reduced_row()] = v;
+    }
   }
   __syncthreads();
 
-  // outputs
-  for (int i = threadIdx.x; i < n_in * rv; i += kThreads) {
-    const int k = i / rv, r = i - k * rv;
-    const int mm = base + k;
-    float acc = s_lam[k] * s_dot[k * rv + r];
-    for (int j = 0; j <= mm; ++j) acc += s_coef[j * n_in + k] * to_f(s_x[j * rv + r]);
-    acc += Dh * to_f(s_x[mm * rv + r]);
-    Io<T>::st((T *)a.y + (((size_t)e * n_in + k) * d.H + h) * d.P + prow0 + r, acc);
+  // outputs: lane = row, one wave per in-flight token, so the loop over
+  // entries is uniform across the wave (D x_m is inside coef[m][k])
+  static_assert(kRows == 64, "one lane per tile row");
+  if (tl.lane < rv) {
+    const int r = tl.lane;
+    T *yr = (T *)a.y + ((size_t)e * n_in * d.H + h) * d.P + prow0 + r;
+    for (int k = __builtin_amdgcn_readfirstlane(tl.wave); k < n_in; k += kThreads / 64) {
+      const int mm = base + k;
+      float acc = s_lam[k] * s_dot[k * rv + r];
+#pragma unroll 4
+      for (int j = 0; j <= mm; ++j) acc += s_coef[j * n_in + k] * to_f(s_x[j * xs + r]);
+      Io<T>::st(yr + (size_t)k * d.H * d.P, acc);
+    }
   }
 }
 
@@ -532,17 +582,16 @@ hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const
   const int pt_n = (a.d.P + 8 * kReplayR - 1) / (8 * kReplayR);
   dim3 grid(a.n * a.d.H * pt_n), block(kThreads);
   const size_t sm = replay_smem_bytes(io, a.W, a.n_in, a.d.N);
-  hipError_t err;
-  if (io == kBF16) {
-    err = allow_lds(replay_kernel<bf16_t, kReplayR>, sm);
-    if (err == hipSuccess)
-      hipLaunchKernelGGL((replay_kernel<bf16_t, kReplayR>), grid, block, sm, s, a, m, lay);
-  } else {
-    err = allow_lds(replay_kernel<float, kReplayR>, sm);
-    if (err == hipSuccess)
-      hipLaunchKernelGGL((replay_kernel<float, kReplayR>), grid, block, sm, s, a, m, lay);
-  }
-  return err == hipSuccess ? hipGetLastError() : err;
+  const bool full = a.d.P % (8 * kReplayR) == 0 && a.d.N == 4 * 32;
+  auto go = [&](auto kernel) {
+    hipError_t err = allow_lds(kernel, sm);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kernel, grid, block, sm, s, a, m, lay);
+    return hipGetLastError();
+  };
+  if (io == kBF16)
+    return full ? go(replay_kernel<bf16_t, kReplayR, true>) : go(replay_kernel<bf16_t, kReplayR, false>);
+  return full ? go(replay_kernel<float, kReplayR, true>) : go(replay_kernel<float, kReplayR, false>);
 }
 
 // ===========================================================================
