@@ -40,7 +40,7 @@ MIB = 1 << 20
 # the kernel sources they were taken on: a change to any of them turns the
 # figure into null until the counters are taken again.
 DECODE_COUNTERS = {
-    "sources": ["ssm_kernels.hip", "ssm_device.h", "ssm_internal.h"],
+    "sources": ["ssm_decode.hip", "ssm_device.h", "ssm_internal.h"],
     "sha256": "cbb0bbe7cfe7f70359edf055d20c161e34b86e78b5f8f45f8ba4420a67f60286",
     "fetch_kib": 519387.49, "write_kib": 1056784.21,
     "calib_fetch_kib": 2059.01, "calib_write_kib": 4096.0, "calib_true_kib": 4096.0,

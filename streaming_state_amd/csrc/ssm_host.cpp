@@ -560,12 +560,9 @@ ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
   for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
     const int n = std::min(kBatchPerLaunch, batch - i0);
     DecodeMeta m;
-    for (int k = 0; k < n; ++k) {
-      const int i = k;
-      m.slot[k] = h_slot_ids[i0 + i];
-      m.ent[k] = (uint16_t)i;
-      m.reset[k] = h_reset ? (h_reset[i0 + i] != 0) : 0;
-    }
+    for (int k = 0; k < n; ++k)
+      m.slot_rst[k] = (uint32_t)h_slot_ids[i0 + k] |
+                      (h_reset && h_reset[i0 + k] ? kDecodeReset : 0u);
     DecodeArgs a{};
     a.x = (const char *)x + (size_t)i0 * d.H * d.P * es;
     a.dt = (const char *)dt + (size_t)i0 * d.H * es;

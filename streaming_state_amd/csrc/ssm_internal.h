@@ -32,10 +32,12 @@ struct Dims {
 };
 
 // ---------------------------------------------------------------- decode
+// Entry k of a launch is row k of x, dt, B, C and y.  One 32-bit word per
+// entry (read through the scalar cache): the slot id in bits 0-30, the reset
+// flag in bit 31.
+constexpr uint32_t kDecodeReset = 0x80000000u;
 struct DecodeMeta {
-  int32_t slot[kBatchPerLaunch];   // in ascending slot order (state locality)
-  uint16_t ent[kBatchPerLaunch];   // batch entry of each slot (rows of x, dt, B, C, y)
-  uint8_t reset[kBatchPerLaunch];
+  uint32_t slot_rst[kBatchPerLaunch];
 };
 struct DecodeArgs {
   const void *x, *dt, *B, *C;  // this launch's first batch entry

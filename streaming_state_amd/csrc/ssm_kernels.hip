@@ -1,6 +1,7 @@
-// ssm_kernels.hip -- gfx950 kernels of the memory-bound paths: batched decode,
+// ssm_kernels.hip -- gfx950 kernels of the memory-bound verify paths:
 // copy-per-draft verify (baseline), ReplaySSM verify with the fused log fold,
-// and the state operations (zero, copy, checksum, finite check).
+// and the state operations (zero, copy, checksum, finite check).  The batched
+// decode kernel is in ssm_decode.hip.
 //
 // All three verify/decode kernels share one shape: a workgroup of 256 threads
 // owns one (batch entry, head, 64-row tile) of the fp32 state, held in
@@ -14,79 +15,6 @@ namespace ssm {
 static __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 static __device__ __forceinline__ float to_f(float v) { return v; }
 static __device__ __forceinline__ float to_f(bf16_t v) { return bf16_to_f(v); }
-
-// ===========================================================================
-// decode: h <- exp(dt A) h + dt x B^T ; y = h C + D x, one token per slot
-// ===========================================================================
-// Decode tiles: R float4 rows per thread (a 256-thread tile covers 8R state
-// rows of one head) and kDecodeTiles consecutive tiles of one slot per
-// workgroup.  On MI355X an in-place read-modify-write sweep is fastest with
-// 16 KiB or 128 KiB per workgroup and slowest with 32-64 KiB.
-constexpr int kDecodeR = 4;
-constexpr int kDecodeTiles = 2;
-
-template <typename T, int R, int TW>
-__global__ __launch_bounds__(kThreads *TW) void decode_kernel(DecodeArgs a, DecodeMeta m) {
-  const TileR<R> tl;
-  const Dims d = a.d;
-  constexpr int kTileRows = 8 * R;
-  const int pt_n = (d.P + kTileRows - 1) / kTileRows;
-  const int tiles_per_entry = d.H * pt_n;
-  const int groups = (tiles_per_entry + TW - 1) / TW;
-  const int k = blockIdx.x / groups;
-  const int tile = (blockIdx.x % groups) * TW + (int)(threadIdx.x / kThreads);
-  if (tile >= tiles_per_entry) return;  // no barriers below: tiles are independent
-  const int pt = tile % pt_n;
-  const int h = tile / pt_n;
-  const int slot = m.slot[k];
-  const int e = m.ent[k];
-  const bool rst = m.reset[k] != 0;
-  const int g = h / (d.H / d.G);
-  const int prow0 = pt * kTileRows;
-  const bool colok = 4 * tl.c < d.N;
-
-  float *st = a.state + (((size_t)slot * d.H + h) * d.P + prow0) * d.N + 4 * tl.c;
-  // state first: the only large read, issued before anything else
-  float4 hv[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const bool ok = colok && (prow0 + tl.row(i) < d.P) && !rst;
-    hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * d.N) : zero4();
-  }
-  const T *x = (const T *)a.x + ((size_t)e * d.H + h) * d.P + prow0;
-  const float dt = Io<T>::ld((const T *)a.dt + (size_t)e * d.H + h);
-  const float dA = expf(dt * a.A[h]);
-  const float Dh = a.D[h];
-  float4 Bv = zero4(), Cv = zero4();
-  if (colok) {
-    Bv = Io<T>::ld4((const T *)a.B + ((size_t)e * d.G + g) * d.N + 4 * tl.c);
-    Cv = Io<T>::ld4((const T *)a.C + ((size_t)e * d.G + g) * d.N + 4 * tl.c);
-  }
-  float part[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const bool rowok = prow0 + tl.row(i) < d.P;
-    const float u = rowok ? dt * Io<T>::ld(x + tl.row(i)) : 0.f;
-    hv[i] = fma4(dA, hv[i], u, Bv);
-    if (rowok && colok) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
-    part[i] = dot4(hv[i], Cv);
-  }
-  const float yv = row_totals<R>(part, tl.lane);
-  const int r = tl.reduced_row();
-  if (tl.reduced_writer() && prow0 + r < d.P)
-    Io<T>::st((T *)a.y + ((size_t)e * d.H + h) * d.P + prow0 + r, yv + Dh * Io<T>::ld(x + r));
-}
-
-hipError_t launch_decode(int io, const DecodeArgs &a, const DecodeMeta &m, hipStream_t s) {
-  constexpr int kTileRows = 8 * kDecodeR;
-  const int tiles = a.d.H * ((a.d.P + kTileRows - 1) / kTileRows);
-  dim3 grid(a.n * ((tiles + kDecodeTiles - 1) / kDecodeTiles)), block(kThreads * kDecodeTiles);
-  if (io == kBF16)
-    hipLaunchKernelGGL((decode_kernel<bf16_t, kDecodeR, kDecodeTiles>), grid, block, 0, s, a, m);
-  else
-    hipLaunchKernelGGL((decode_kernel<float, kDecodeR, kDecodeTiles>), grid, block, 0, s, a, m);
-  return hipGetLastError();
-}
 
 // ===========================================================================
 // copy-per-draft verify: read once, then per token update, write a full copy,
