@@ -227,8 +227,9 @@ __device__ __forceinline__ float sum32_dpp(float v) {
 // reach the next integer).  d = 1 is passed through (its multiplier would be 2^32).
 struct FastDiv {
   uint32_t d, m;
-  __device__ __forceinline__ explicit FastDiv(int dv)
-      : d((uint32_t)dv), m(dv > 1 ? 0xffffffffu / (uint32_t)dv + 1u : 0u) {}
+  __device__ __forceinline__ explicit FastDiv(int dv) : d((uint32_t)dv), m(fastdiv_magic(dv)) {}
+  // with the multiplier computed by the host (fastdiv_magic)
+  __device__ __forceinline__ FastDiv(int dv, uint32_t mv) : d((uint32_t)dv), m(mv) {}
   __device__ __forceinline__ int div(int i) const {
     return d > 1 ? (int)__umulhi((uint32_t)i, m) : i;
   }

@@ -220,9 +220,7 @@ ssm_status fold_logs(Handle *H, const std::vector<int> &slots, hipStream_t s) {
     for (int i = 0; i < n; ++i) {
       Slot &sl = H->slots[slots[i0 + i]];
       m.slot[i] = slots[i0 + i];
-      m.fold_len[i] = (uint8_t)sl.log_len;
-      m.base_len[i] = 0;
-      m.halves[i] = (uint8_t)(sl.log_half | ((1 - sl.log_half) << 1));
+      m.info[i] = replay_info(sl.log_len, 0, sl.log_half, 1 - sl.log_half);
     }
     ReplayArgs a{};
     a.state = H->state;
@@ -234,6 +232,7 @@ ssm_status fold_logs(Handle *H, const std::vector<int> &slots, hipStream_t s) {
     a.n = n;
     a.n_in = 0;
     a.W = H->W;
+    a.nin_magic = fastdiv_magic(a.n_in);
     HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
   }
   for (int sidx : slots) {
@@ -654,15 +653,10 @@ ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
     for (int i = 0; i < n; ++i) {
       const Slot &sl = H->slots[h_slot_ids[i0 + i]];
       m.slot[i] = h_slot_ids[i0 + i];
-      if (sl.log_len + n_in > H->W) {  // the log is full: fold, then start the other half
-        m.fold_len[i] = (uint8_t)sl.log_len;
-        m.base_len[i] = 0;
-        m.halves[i] = (uint8_t)(sl.log_half | ((1 - sl.log_half) << 1));
-      } else {
-        m.fold_len[i] = 0;
-        m.base_len[i] = (uint8_t)sl.log_len;
-        m.halves[i] = (uint8_t)(sl.log_half | (sl.log_half << 1));
-      }
+      if (sl.log_len + n_in > H->W)  // the log is full: fold, then start the other half
+        m.info[i] = replay_info(sl.log_len, 0, sl.log_half, 1 - sl.log_half);
+      else
+        m.info[i] = replay_info(0, sl.log_len, sl.log_half, sl.log_half);
     }
     const size_t off = (size_t)i0 * n_in;
     ReplayArgs a{};
@@ -680,6 +674,7 @@ ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
     a.n = n;
     a.n_in = n_in;
     a.W = H->W;
+    a.nin_magic = fastdiv_magic(a.n_in);
     HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
   }
   for (int i = 0; i < batch; ++i) {

@@ -66,12 +66,29 @@ struct CopyArgs {
 hipError_t launch_copy(int io, const CopyArgs &a, const CopyMeta &m, hipStream_t s);
 
 // ------------------------------------------------------------------ replay
+// Per entry: the slot and one 32-bit word (read through the scalar cache) with
+// the entries folded into the checkpoint first (bits 0-7, 0: none), the
+// committed entries the in-flight tokens follow (bits 8-15), the half read by
+// the fold (bit 16) and the half of the live log (bit 17).
 struct ReplayMeta {
   int32_t slot[kBatchPerLaunch];
-  uint8_t fold_len[kBatchPerLaunch];  // entries folded into the checkpoint first (0: none)
-  uint8_t base_len[kBatchPerLaunch];  // committed entries the in-flight tokens follow
-  uint8_t halves[kBatchPerLaunch];    // bit0: half read by the fold; bit1: half of the live log
+  uint32_t info[kBatchPerLaunch];
 };
+__host__ __device__ inline uint32_t replay_info(int fold_len, int base_len, int fold_half,
+                                                int live_half) {
+  return (uint32_t)fold_len | (uint32_t)base_len << 8 | (uint32_t)fold_half << 16 |
+         (uint32_t)live_half << 17;
+}
+__host__ __device__ inline int info_fold(uint32_t u) { return (int)(u & 0xffu); }
+__host__ __device__ inline int info_base(uint32_t u) { return (int)((u >> 8) & 0xffu); }
+__host__ __device__ inline int info_fold_half(uint32_t u) { return (int)((u >> 16) & 1u); }
+__host__ __device__ inline int info_live_half(uint32_t u) { return (int)((u >> 17) & 1u); }
+// Multiplier of the kernels' division by a small divisor d (FastDiv):
+// ceil(2^32 / d) for d > 1.
+__host__ __device__ inline uint32_t fastdiv_magic(int d) {
+  return d > 1 ? 0xffffffffu / (uint32_t)d + 1u : 0u;
+}
+
 struct ReplayArgs {
   const void *x, *dt, *B, *C;  // [n, n_in, ...] for this launch
   void *y;
@@ -81,6 +98,7 @@ struct ReplayArgs {
   const float *A, *D;
   Dims d;
   int n, n_in, W;
+  uint32_t nin_magic;          // fastdiv_magic(n_in)
 };
 // Log layout: three arrays, each [S][2 halves][W entries][...] in the io dtype
 // (dt: [H], x: [H*P], B: [G*N]), then fp32 B.C scratch.

@@ -129,10 +129,11 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
                                                              LogLayout lay) {
   extern __shared__ float4 bc_smem[];
   const Dims d = a.d;
-  const int e = blockIdx.x / d.G, g = blockIdx.x % d.G;
+  const int g = blockIdx.x, e = blockIdx.y;
   const int slot = m.slot[e];
-  const int base = m.base_len[e];
-  const int wh = (m.halves[e] >> 1) & 1;
+  const uint32_t info = m.info[e];
+  const int base = info_base(info);
+  const int wh = info_live_half(info);
   const int n_in = a.n_in, J = base + n_in;
   const int q = d.N >> 2, qs = q + 1;
   float4 *sB = bc_smem;                    // [J][qs]
@@ -282,34 +283,31 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   constexpr int E = 16 / (int)sizeof(T);  // io elements per 16-byte chunk
   const Dims d = a.d;
   const int W = a.W, n_in = a.n_in;
-  const int pt_n = (d.P + kRows - 1) / kRows;
-  int bid = blockIdx.x;
-  const int pt = bid % pt_n;
-  bid /= pt_n;
-  const int h = bid % d.H;
-  const int e = bid / d.H;
+  const int N = kFull ? 4 * 32 : d.N;
+  const int pt = blockIdx.x, h = blockIdx.y, e = blockIdx.z;
   const int slot = m.slot[e];
-  const int F = m.fold_len[e];
-  const int base = m.base_len[e];
-  const int rh = m.halves[e] & 1, wh = (m.halves[e] >> 1) & 1;
+  const uint32_t info = m.info[e];
+  const int F = info_fold(info);
+  const int base = info_base(info);
+  const int rh = info_fold_half(info), wh = info_live_half(info);
   const int J = base + n_in;
-  const int g = h / (d.H / d.G);
+  const int g = d.G == 1 ? 0 : h / (d.H / d.G);
   const int prow0 = pt * kRows;
-  const int rv = min(kRows, d.P - prow0);  // rows of this tile inside the head
-  const bool whole_chunks = (d.P * (int)sizeof(T)) % 16 == 0 && (d.N * (int)sizeof(T)) % 16 == 0 &&
+  const int rv = kFull ? kRows : min(kRows, d.P - prow0);  // rows of this tile inside the head
+  const bool whole_chunks = (d.P * (int)sizeof(T)) % 16 == 0 && (N * (int)sizeof(T)) % 16 == 0 &&
                             (((uintptr_t)a.x | (uintptr_t)a.C) & 15) == 0;
   // LDS stride of an entry's x rows: rv for whole chunks (the copies are
   // contiguous), else rounded up so that every 8-row group starts 16-byte aligned
   const int xs = whole_chunks ? rv : (rv + 7) & ~7;
-  const bool colok = 4 * tl.c < d.N;
-  const size_t PN = (size_t)d.P * d.N;
+  const bool colok = 4 * tl.c < N;
+  const size_t PN = (size_t)d.P * N;
   const float Ah = a.A[h], Dh = a.D[h];
   const LogIdx li{W};
   T *logdt = (T *)((char *)a.log + lay.dt_off);
   T *logx = (T *)((char *)a.log + lay.x_off);
   const T *logB = (const T *)((const char *)a.log + lay.B_off);
   const T *inx = (const T *)a.x, *indt = (const T *)a.dt, *inC = (const T *)a.C;
-  const ReplaySmem L(W, n_in, d.N, rv, (int)sizeof(T));
+  const ReplaySmem L(W, n_in, N, rv, (int)sizeof(T));
   T *s_V = (T *)(sb + L.V);  // [F + n_in][N]
   T *s_x = (T *)(sb + L.x);  // [J + F][xs]
   float *s_dt = (float *)(sb + L.dt), *s_fdt = (float *)(sb + L.fdt);
@@ -321,14 +319,14 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   // and the in-flight x, the fold entries' x, the fold B rows and the
   // in-flight C rows.  Consecutive log entries of a slot and half are
   // consecutive in the log, so every run is (first row, stride, count).
-  const size_t xstride = (size_t)d.H * d.P, vstride = (size_t)d.G * d.N;
+  const size_t xstride = (size_t)d.H * d.P, vstride = (size_t)d.G * N;
   const T *x_com = logx + (li.ent(slot, wh, 0) * d.H + h) * d.P + prow0;
   const T *x_new = inx + ((size_t)e * n_in * d.H + h) * d.P + prow0;
   const T *x_fold = logx + (li.ent(slot, rh, 0) * d.H + h) * d.P + prow0;
-  const T *b_fold = logB + li.ent(slot, rh, 0) * vstride + (size_t)g * d.N;
-  const T *c_new = inC + (size_t)e * n_in * vstride + (size_t)g * d.N;
+  const T *b_fold = logB + li.ent(slot, rh, 0) * vstride + (size_t)g * N;
+  const T *c_new = inC + (size_t)e * n_in * vstride + (size_t)g * N;
   if (whole_chunks) {
-    const int cx = rv / E, cv = d.N / E;
+    const int cx = rv / E, cv = N / E;
     const FastDiv fx(cx), fv(cv);
     auto run = [&](char *lds, const T *src, size_t stride, int rows, int chunks, FastDiv f) {
       stage_lds(lds, rows * chunks, [&](int i) {
@@ -340,34 +338,34 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
     run(sb + L.x + base * xs * (int)sizeof(T), x_new, xstride, n_in, cx, fx);
     run(sb + L.x + J * xs * (int)sizeof(T), x_fold, xstride, F, cx, fx);
     run(sb + L.V, b_fold, vstride, F, cv, fv);
-    run(sb + L.V + F * d.N * (int)sizeof(T), c_new, vstride, n_in, cv, fv);
+    run(sb + L.V + F * N * (int)sizeof(T), c_new, vstride, n_in, cv, fv);
   } else {  // rows not made of aligned 16-byte chunks: element copies
-    const FastDiv frv(rv), fn(d.N);
+    const FastDiv frv(rv), fn(N);
     for (int i = threadIdx.x; i < (J + F) * rv; i += kThreads) {
       const int j = frv.div(i), r = i - j * rv;
       const T *src = j >= J ? x_fold + (j - J) * xstride
                      : j < base ? x_com + j * xstride : x_new + (j - base) * xstride;
       s_x[j * xs + r] = src[r];
     }
-    for (int i = threadIdx.x; i < (F + n_in) * d.N; i += kThreads) {
+    for (int i = threadIdx.x; i < (F + n_in) * N; i += kThreads) {
       const int r = fn.div(i);
-      s_V[i] = (r < F ? b_fold + r * vstride : c_new + (r - F) * vstride)[i - r * d.N];
+      s_V[i] = (r < F ? b_fold + r * vstride : c_new + (r - F) * vstride)[i - r * N];
     }
   }
 
   // checkpoint tile
-  float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * d.N + 4 * tl.c;
+  float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * N + 4 * tl.c;
   float4 hv[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const bool ok = colok && (tl.row(i) < rv);
-    hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * d.N) : zero4();
+    hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * N) : zero4();
   }
 
   // scalars: combined dt, fold dt, B.C products
   const float *bc = a.bc + ((size_t)e * d.G + g) * W * kMaxInFlight;
   const int nS = J + F + J * n_in;
-  const FastDiv fnin(n_in);
+  const FastDiv fnin(n_in, a.nin_magic);
   const T *dt_com = logdt + li.ent(slot, wh, 0) * d.H + h;
   const T *dt_new = indt + (size_t)e * n_in * d.H + h;
   const T *dt_fold = logdt + li.ent(slot, rh, 0) * d.H + h;
@@ -425,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   __syncthreads();
 
   // fold, then ckpt . C_k for every in-flight token
-  const T *s_C = s_V + F * d.N;
+  const T *s_C = s_V + F * N;
   {
     const bool ck = kFull || colok;
     if (F > 0) {
@@ -436,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
       const T *fx = s_x + J * xs + tl.row(0);  // this lane's R consecutive rows
 #pragma unroll 1
       for (int j = 0; j < F; ++j) {
-        const float4 Bv = ck ? lds_ld4(s_V + j * d.N + 4 * tl.c) : zero4();
+        const float4 Bv = ck ? lds_ld4(s_V + j * N + 4 * tl.c) : zero4();
         const float w = s_fw[j];
         float xv[R];
         lds_ld_rows<T, R>(fx + j * xs, xv);
@@ -446,10 +444,10 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
       }
 #pragma unroll
       for (int i = 0; i < R; ++i)
-        if (ck && (kFull || tl.row(i) < rv)) nt_store4(st + (size_t)tl.row(i) * d.N, hv[i]);
+        if (ck && (kFull || tl.row(i) < rv)) nt_store4(st + (size_t)tl.row(i) * N, hv[i]);
     }
     for (int k = 0; k < n_in; ++k) {
-      const float4 Cv = ck ? lds_ld4(s_C + k * d.N + 4 * tl.c) : zero4();
+      const float4 Cv = ck ? lds_ld4(s_C + k * N + 4 * tl.c) : zero4();
       float part[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) part[i] = dot4(hv[i], Cv);
@@ -494,7 +492,7 @@ template <typename K> static hipError_t allow_lds(K kernel, size_t bytes) {
 hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const LogLayout &lay,
                          hipStream_t s) {
   if (a.n_in > 0) {
-    dim3 g1(a.n * a.d.G), b1(kThreads);
+    dim3 g1(a.d.G, a.n), b1(kThreads);
     const size_t sm1 = replay_bc_smem_bytes(a.W, a.n_in, a.d.N);
     hipError_t err;
     if (io == kBF16) {
@@ -508,7 +506,7 @@ hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const
     if (err != hipSuccess) return err;
   }
   const int pt_n = (a.d.P + 8 * kReplayR - 1) / (8 * kReplayR);
-  dim3 grid(a.n * a.d.H * pt_n), block(kThreads);
+  dim3 grid(pt_n, a.d.H, a.n), block(kThreads);
   const size_t sm = replay_smem_bytes(io, a.W, a.n_in, a.d.N);
   const bool full = a.d.P % (8 * kReplayR) == 0 && a.d.N == 4 * 32;
   auto go = [&](auto kernel) {
