@@ -41,8 +41,8 @@ MIB = 1 << 20
 # figure into null until the counters are taken again.
 DECODE_COUNTERS = {
     "sources": ["ssm_decode.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "cbb0bbe7cfe7f70359edf055d20c161e34b86e78b5f8f45f8ba4420a67f60286",
-    "fetch_kib": 519387.49, "write_kib": 1056784.21,
+    "sha256": "74e9a1112cb7647d4691763fb9f0d14506481a6b4fdd70c307ffc2f72672107e",
+    "fetch_kib": 519888.69, "write_kib": 1056770.73,
     "calib_fetch_kib": 2059.01, "calib_write_kib": 4096.0, "calib_true_kib": 4096.0,
     "algorithmic_kib": 1035989.33 + 1056768.0,
 }
@@ -54,11 +54,21 @@ DECODE_COUNTERS = {
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
     "sources": ["ssm_ssd.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "829d66e195aa6b6c044a77a179e216c18a492967f06eec8ad0cdd1fd44fb5fce",
-    "mfma_busy_cycles": 420020224.0, "gui_active_cycles": 19989437.75, "xcds": 8, "simds": 1024,
+    "sha256": "dcb2361100bbed7cff246ff0d9b143e50bbf9312b6497ab9d9f7bb99f4601550",
+    "mfma_busy_cycles": 420020224.0, "gui_active_cycles": 19655994.67, "xcds": 8, "simds": 1024,
     "mfma_mops_bf16": 840040448.0,
-    "fetch_kib": 738667.48, "write_kib": 1085440.71,
+    "fetch_kib": 740561.95, "write_kib": 1085440.93,
     "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2**25 + 2 * 2**22,
+}
+
+# The same for replay_kernel at W = 16 (mean over the 6 verify steps of
+# "--only replay --steps 5 --warmup 1"; the algorithmic bytes of exactly those
+# steps, from the log lengths, averaged).
+REPLAY_COUNTERS = {
+    "sources": ["ssm_kernels.hip", "ssm_device.h", "ssm_internal.h"],
+    "sha256": "d3f5df0d206cce720595115d8689ea3c5ccdc2a312157a5b3d26342a1fcf0f88",
+    "fetch_kib": 577234.83, "write_kib": 208579.74,
+    "algorithmic_bytes": 1375888554.67,
 }
 
 
@@ -84,6 +94,17 @@ def prefill_counters():
             "mfma_flops_executed": c["mfma_mops_bf16"] * 512,
             "traffic": round(kib * 1024),
             "traffic_over_algorithmic": round(kib * 1024 / c["algorithmic_bytes"], 4)}
+
+
+def replay_counter_traffic():
+    """Scaled HBM bytes per replay_kernel launch over its algorithmic bytes,
+    or None if the kernel changed since the counters were taken."""
+    c, d = REPLAY_COUNTERS, DECODE_COUNTERS
+    if not _sources_match(c):
+        return None
+    kib = (c["fetch_kib"] * d["calib_true_kib"] / d["calib_fetch_kib"]
+           + c["write_kib"] * d["calib_true_kib"] / d["calib_write_kib"])
+    return round(kib * 1024 / c["algorithmic_bytes"], 4)
 
 
 def counter_traffic():
@@ -222,7 +243,7 @@ def main():
     pre_seq = [0]
     flushes_before = 0
 
-    rep_bytes = []
+    rep_bytes, rep_bytes_all = [], []
     entry_b = (H + H * P + G * N) * 4   # one log entry: dt[H], x[H,P], B[G,N]
     io_b = n_in * (2 * H * P + H + 2 * G * N) * 4  # in-flight x, dt, B, C in; y out
 
@@ -251,8 +272,10 @@ def main():
         a = acc_all[s % len(acc_all)]
         sp = spec_in[s % len(spec_in)]
         if rep16 is not None:
-            if timed:  # algorithmic bytes of this verify step, from the log lengths
-                rep_bytes.append(replay_bytes(rep16, slots3, 16))
+            # algorithmic bytes of this verify step, from the log lengths
+            rep_bytes_all.append(replay_bytes(rep16, slots3, 16))
+            if timed:
+                rep_bytes.append(rep_bytes_all[-1])
             e = t_rep.start() if timed else None
             rep16.replay_step(slots3, *sp, y=y_spec)
             if timed:
@@ -300,7 +323,10 @@ def main():
         comp["replay_W16"] = dict(ms_mean=float(ms.mean()), ms_median=float(np.median(ms)),
                                   flushes=int(rep16.counters()["replay_flushes"] - flushes_before),
                                   bytes_per_step=float(np.mean(rep_bytes)),
-                                  GBps=float(np.mean(rep_bytes) / (ms.mean() * 1e-3) / 1e9))
+                                  GBps=float(np.mean(rep_bytes) / (ms.mean() * 1e-3) / 1e9),
+                                  bytes_each_step_with_warmup=[int(b) for b in rep_bytes_all],
+                                  frac_hbm=float(np.mean(rep_bytes) / (ms.mean() * 1e-3) / 8e12),
+                                  traffic_over_algorithmic_counters=replay_counter_traffic())
     if cop is not None:
         ms = np.array(t_cop.ms())
         cbytes = Bd * state_b * (1 + n_in) + Bd * n_in * (H * P * 8 + H * 4 + 2 * G * N * 4)
