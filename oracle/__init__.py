@@ -9,7 +9,9 @@ HIP library (``streaming_state_amd``); neither imports the other.
 module only marshals numpy arrays into it.  ``acceptance.py`` and
 ``schedule.py`` hold the integer/host-side model of speculative decoding and
 of the replay flush schedule; ``blob.py`` reads and writes the state-blob byte
-format of the recurrent-state companion store.
+format of the recurrent-state companion store; ``conv.py`` holds the causal
+depthwise conv1d with its carried conv state and the gated output (numpy,
+fp64).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against the pages and
 the mathematics (worked example, closed forms, brute force); none is "parity
