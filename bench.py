@@ -157,8 +157,9 @@ class Timer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path shards by batch or head with no exchange; see DESIGN.md)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(decode and replay would shard by batch or head with no exchange; one GPU's "
+              "share is the workload measured here)",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -406,6 +407,7 @@ def main():
                                        host_wall_us_per_call=wall1 * 1e6 / len(sizes))
         extras["stream_130m"] = stream1
         extras["replay_alone_vs_decode"] = replay_alone_sweep(torch, ssm, inputs, H, P, N, G, dev)
+        extras["conv_and_gate"] = conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev)
         # plain device copy of 1 GiB for the achievable-bandwidth context
         a = torch.empty(256 * MIB, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -464,6 +466,65 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
+
+
+def conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev, reps=10):
+    """The steps around the scan at the workloads' shapes: the conv over the
+    packed prefill (65,536 bf16 tokens, C = H*P + 2*G*N channels, K = 4, a
+    reset at each sequence start), the conv decode step for 256 slots (fp32),
+    and the gated group RMS norm over the prefill's y (bf16, one group of H*P
+    channels).  Algorithmic bytes: every input read once and every output and
+    state written once."""
+    C, K, L, Bd = H * P + 2 * G * N, 4, 65536, 256
+    A, D = inputs.params(4, H)
+    At, Dt = torch.from_numpy(A).to(dev), torch.from_numpy(D).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    w = torch.randn((C, K), generator=g, device=dev) * 0.5
+    b = torch.randn(C, generator=g, device=dev) * 0.1
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def line(ms, nbytes):
+        return dict(ms=ms, bytes=int(nbytes), GBps=nbytes / (ms * 1e-3) / 1e9,
+                    frac_hbm=nbytes / (ms * 1e-3) / 8e12)
+
+    out = {"channels": C, "K": K}
+    h = ssm.StreamState(H, P, N, 1, At, Dt, G=G, io_dtype="bf16")
+    h.conv_attach(C, K, w, b, act=True)
+    x = torch.randn((L, C), generator=g, device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    lengths = inputs.sequence_lengths()
+    rs = np.zeros(L, np.uint8)
+    rs[np.concatenate([[0], np.cumsum(lengths)[:-1]])] = 1
+    ms = timed(lambda: h.conv_chunk(0, x, reset=rs, y=y))
+    out["conv_chunk_prefill"] = line(ms, 2 * L * C * 2 + 2 * C * (K - 1) * 4 + C * (K + 1) * 4)
+    # gated RMS norm over y[L, H*P] with z of the same shape
+    yz = torch.randn((2, L, H * P), generator=g, device=dev).to(torch.bfloat16)
+    nw = torch.randn(H * P, generator=g, device=dev)
+    og = torch.empty_like(yz[0])
+    ms = timed(lambda: ssm.gate(yz[0], yz[1], nw, group=H * P, out=og))
+    out["gate_norm_prefill"] = line(ms, 3 * L * H * P * 2 + H * P * 4)
+    del x, y, yz, og
+    h.destroy()
+    hd = ssm.StreamState(H, P, N, Bd, At, Dt, G=G)
+    hd.conv_attach(C, K, w, b, act=True)
+    xd = torch.randn((Bd, C), generator=g, device=dev)
+    yd = torch.empty_like(xd)
+    slots = np.arange(Bd, dtype=np.int32)
+    ms = timed(lambda: hd.conv_decode(slots, xd, y=yd))
+    out["conv_decode_256"] = line(ms, 2 * Bd * C * (K - 1) * 4 + 2 * Bd * C * 4 + C * (K + 1) * 4)
+    hd.destroy()
+    return out
 
 
 def replay_alone_sweep(torch, ssm, inputs, H, P, N, G, dev, W=16, steps=32, warm=16):

@@ -307,6 +307,54 @@ ssm_status ssm_state_serialize(ssm_handle h, int32_t slot, void *h_blob, size_t 
 ssm_status ssm_state_deserialize(ssm_handle h, int32_t slot, const void *h_blob, size_t len,
                                  const ssm_receipt *r, void *stream);
 
+/* -------------------------------------------- conv1d and the gated output */
+/* The steps on either side of the scan.  The pages name the conv state as half
+ * of a Mamba layer's recurrent state (the state blob of "SSM.PREFIX.* --
+ * recurrent-state companion" lists [conv_state, ssm_state]) but define
+ * neither step; these are the Mamba-2 block's:
+ *   conv:  y[t,c] = act(b[c] + sum_{k<K} w[c,k] * x[t-(K-1)+k, c]), tap K-1 on
+ *          the current token, act = SiLU (v * sigmoid(v)) or the identity;
+ *   state: per slot and channel, the K-1 inputs before the next token, oldest
+ *          first, fp32 [S, C, K-1]; a reset on token t hides every input
+ *          before t, as for the scan;
+ *   gate:  g = y * SiLU(z), then optionally each group of channels divided
+ *          by its root mean square and scaled by a weight. */
+
+/* Bytes of the conv state for n_slots slots: n_slots * C * (K-1) * 4, or 0
+ * for a bad shape. */
+size_t ssm_conv_state_bytes(int32_t n_slots, int32_t C, int32_t K);
+
+/* Attach a causal depthwise conv of C channels and width K (1 <= K <= 4) to
+ * the handle: d_conv_state[S, C, K-1] (device fp32, caller-owned; NULL when
+ * K = 1), d_w[C, K] and d_bias[C] or NULL (device fp32; they must outlive the
+ * handle), act 1 for SiLU, 0 for none.  The state memory is not touched:
+ * ssm_state_reset / ssm_state_init clear both the conv state and the scan
+ * state of a slot from now on. */
+ssm_status ssm_conv_attach(ssm_handle h, int32_t C, int32_t K, int32_t act, float *d_conv_state,
+                           const float *d_w, const float *d_bias);
+
+/* The conv over one chunk of `slot`'s stream: x[L, C] in, y[L, C] out
+ * (device, the handle's io dtype; y must not overlap x), h_reset host u8[L]
+ * or NULL.  The slot's conv state is the carry-in and receives the carry-out,
+ * so a stream cut into chunks gives the outputs of the whole stream.  Call
+ * it once per chunk, in order, with the chunk's reset flags (the conv keeps
+ * no sequence numbers of its own). */
+ssm_status ssm_conv_chunk(ssm_handle h, int32_t slot, int64_t L, const void *x,
+                          const uint8_t *h_reset, void *y, void *stream);
+
+/* One token for each of `batch` distinct slots: x[batch, C] in, y[batch, C]
+ * out; h_reset host u8[batch] or NULL (a set flag starts the slot's conv
+ * window empty). */
+ssm_status ssm_conv_decode(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, const void *x,
+                           const uint8_t *h_reset, void *y, void *stream);
+
+/* Gated output over rows x C (device, io_dtype SSM_F32 or SSM_BF16):
+ * out = y * SiLU(z); with d_norm_w[C] (device fp32) non-NULL, each group of
+ * `group` channels (group divides C) is then divided by
+ * sqrt(mean(g^2) + eps) and multiplied by d_norm_w.  out may be y. */
+ssm_status ssm_gate(int32_t io_dtype, int64_t rows, int32_t C, int32_t group, const void *y,
+                    const void *z, const float *d_norm_w, float eps, void *out, void *stream);
+
 /* Read a slot's position and next expected chunk sequence number. */
 ssm_status ssm_get_position(ssm_handle h, int32_t slot, int64_t *pos, uint64_t *chunk_seq);
 

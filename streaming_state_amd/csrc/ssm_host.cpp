@@ -68,11 +68,16 @@ struct Handle {
   // copy baseline
   int n_in_max = 0;
   float *copies = nullptr;
+  // causal conv before the scan (0 channels: not attached)
+  int conv_C = 0, conv_K = 0, conv_act = 0;
+  float *conv_state = nullptr;  // [S, C, K-1]
+  const float *conv_w = nullptr, *conv_b = nullptr;
   // device scratch: [0] checksum accumulator (u64), [1] finite flag (u32)
   void *scratch = nullptr;
   ssm_counters cnt{};
   size_t state_bytes() const { return (size_t)d.H * d.P * d.N * sizeof(float); }
   float *slot_state(int s) const { return state + (size_t)s * d.H * d.P * d.N; }
+  size_t conv_floats() const { return (size_t)conv_C * (conv_K > 0 ? conv_K - 1 : 0); }
 };
 
 std::mutex g_mu;
@@ -345,6 +350,8 @@ static ssm_status reset_or_init(ssm_handle h, int32_t n, const int32_t *slots, c
       HIP_TRY(launch_copy_f32(H->slot_state(slots[i]), init + (size_t)i * nf, nf, s));
     else
       HIP_TRY(launch_zero(H->slot_state(slots[i]), nf, s));
+    if (H->conv_floats())  // both halves of the slot's state start fresh
+      HIP_TRY(launch_zero(H->conv_state + (size_t)slots[i] * H->conv_floats(), H->conv_floats(), s));
   }
   for (int i = 0; i < n; ++i) fresh_stream(H->slots[slots[i]]);
   H->cnt.resets += n;
@@ -1135,6 +1142,143 @@ ssm_status ssm_state_deserialize(ssm_handle h, int32_t slot, const void *h_blob,
                          hipMemcpyHostToDevice, s));
   HIP_TRY(hipStreamSynchronize(s));
   adopt_receipt(H, slot, r);
+  return SSM_OK;
+}
+
+// --------------------------------------------------- conv1d and gated output
+size_t ssm_conv_state_bytes(int32_t n_slots, int32_t C, int32_t K) {
+  if (n_slots < 1 || C < 1 || K < 1 || K > kMaxConvK) return 0;
+  return (size_t)n_slots * C * (K - 1) * sizeof(float);
+}
+
+ssm_status ssm_conv_attach(ssm_handle h, int32_t C, int32_t K, int32_t act, float *d_conv_state,
+                           const float *d_w, const float *d_bias) {
+  GET_HANDLE(H, h);
+  if (C < 1 || K < 1 || K > kMaxConvK)
+    return fail(SSM_E_INVALID_ARG, "conv: need C >= 1 and 1 <= K <= %d (C=%d K=%d)", kMaxConvK,
+                C, K);
+  if (act != 0 && act != 1) return fail(SSM_E_INVALID_ARG, "conv: act must be 0 or 1");
+  if (!d_w || (K > 1 && !d_conv_state))
+    return fail(SSM_E_INVALID_ARG, "conv: weights and (for K > 1) the conv state are required");
+  if (!aligned(d_w, 4) || !aligned(d_conv_state, 4) || !aligned(d_bias, 4))
+    return fail(SSM_E_INVALID_ARG, "conv: misaligned weight, bias or state pointer");
+  H->conv_C = C;
+  H->conv_K = K;
+  H->conv_act = act;
+  H->conv_state = K > 1 ? d_conv_state : nullptr;
+  H->conv_w = d_w;
+  H->conv_b = d_bias;
+  return SSM_OK;
+}
+
+namespace {
+
+ConvArgs conv_args(const Handle *H) {
+  ConvArgs a{};
+  a.w = H->conv_w;
+  a.bias = H->conv_b;
+  a.C = H->conv_C;
+  a.K = H->conv_K;
+  a.act = H->conv_act;
+  return a;
+}
+
+// Tokens per conv launch: bounded by the grid's y extent (runs of 8 tokens).
+constexpr int64_t kConvTokensPerLaunch = 1 << 18;
+
+}  // namespace
+
+ssm_status ssm_conv_chunk(ssm_handle h, int32_t slot, int64_t L, const void *x,
+                          const uint8_t *h_reset, void *y, void *stream) {
+  GET_HANDLE(H, h);
+  if (!H->conv_C) return fail(SSM_E_INVALID_STATE, "conv: no conv attached");
+  if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "conv: bad slot %d", slot);
+  if (L < 0 || L > INT32_MAX) return fail(SSM_E_INVALID_ARG, "conv: bad chunk length");
+  if (L == 0) return SSM_OK;
+  if (!x || !y) return fail(SSM_E_INVALID_ARG, "conv: NULL input or output");
+  const size_t es = io_size(H->io);
+  if (!aligned(x, es) || !aligned(y, es)) return fail(SSM_E_INVALID_ARG, "conv: misaligned x or y");
+  const size_t bytes = (size_t)L * H->conv_C * es;
+  if ((const char *)x < (const char *)y + bytes && (const char *)y < (const char *)x + bytes)
+    return fail(SSM_E_INVALID_ARG, "conv: x and y overlap");
+  hipStream_t s = as_stream(stream);
+  ssm_status st = check_finite(H, s, {{x, (size_t)L * H->conv_C}});
+  if (st != SSM_OK) return st;
+  std::vector<int32_t> rst;
+  if (h_reset)
+    for (int64_t t = 0; t < L; ++t)
+      if (h_reset[t]) rst.push_back((int32_t)t);
+  ConvArgs a = conv_args(H);
+  a.x = x;
+  a.y = y;
+  a.state = H->conv_state ? H->conv_state + (size_t)slot * H->conv_floats() : nullptr;
+  const int none = -H->conv_K;  // no reset yet: the carried state is visible
+  size_t ri = 0;
+  int first = none;
+  for (int64_t t0 = 0; t0 < L;) {
+    // a piece holds at most kConvResetsPerLaunch resets and kConvTokensPerLaunch tokens
+    int64_t t1 = std::min(L, t0 + kConvTokensPerLaunch);
+    if (rst.size() - ri > (size_t)kConvResetsPerLaunch && rst[ri + kConvResetsPerLaunch] < t1)
+      t1 = rst[ri + kConvResetsPerLaunch];
+    ConvChunkMeta m{};
+    m.first_before = first;
+    while (ri < rst.size() && rst[ri] < t1) {
+      m.rst[m.n_rst++] = rst[ri];
+      first = rst[ri++];
+    }
+    a.t_begin = (int)t0;
+    a.t_end = (int)t1;
+    HIP_TRY(launch_conv_chunk(H->io, a, m, s));
+    t0 = t1;
+  }
+  HIP_TRY(launch_conv_state(H->io, a, (int)L, first, s));
+  return SSM_OK;
+}
+
+ssm_status ssm_conv_decode(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, const void *x,
+                           const uint8_t *h_reset, void *y, void *stream) {
+  GET_HANDLE(H, h);
+  if (!H->conv_C) return fail(SSM_E_INVALID_STATE, "conv: no conv attached");
+  ssm_status st = check_slots(H, batch, h_slot_ids, "conv decode");
+  if (st != SSM_OK) return st;
+  if (batch == 0) return SSM_OK;
+  if (!x || !y) return fail(SSM_E_INVALID_ARG, "conv decode: NULL input or output");
+  const size_t es = io_size(H->io);
+  if (!aligned(x, es) || !aligned(y, es))
+    return fail(SSM_E_INVALID_ARG, "conv decode: misaligned x or y");
+  hipStream_t s = as_stream(stream);
+  st = check_finite(H, s, {{x, (size_t)batch * H->conv_C}});
+  if (st != SSM_OK) return st;
+  for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
+    const int n = std::min(kBatchPerLaunch, batch - i0);
+    DecodeMeta m;
+    for (int k = 0; k < n; ++k)
+      m.slot_rst[k] = (uint32_t)h_slot_ids[i0 + k] |
+                      (h_reset && h_reset[i0 + k] ? kDecodeReset : 0u);
+    ConvArgs a = conv_args(H);
+    a.x = (const char *)x + (size_t)i0 * H->conv_C * es;
+    a.y = (char *)y + (size_t)i0 * H->conv_C * es;
+    a.state = H->conv_state;
+    a.n = n;
+    HIP_TRY(launch_conv_decode(H->io, a, m, s));
+  }
+  return SSM_OK;
+}
+
+ssm_status ssm_gate(int32_t io_dtype, int64_t rows, int32_t C, int32_t group, const void *y,
+                    const void *z, const float *d_norm_w, float eps, void *out, void *stream) {
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16)
+    return fail(SSM_E_INVALID_ARG, "gate: io dtype must be SSM_F32 or SSM_BF16");
+  if (rows < 0 || rows > INT32_MAX || C < 1) return fail(SSM_E_INVALID_ARG, "gate: bad shape");
+  if (d_norm_w && (group < 1 || C % group != 0 || C / group > 65535))
+    return fail(SSM_E_INVALID_ARG, "gate: group must divide C (at most 65535 groups)");
+  if (d_norm_w && !(eps >= 0.f)) return fail(SSM_E_INVALID_ARG, "gate: eps must be >= 0");
+  if (rows == 0) return SSM_OK;
+  if (!y || !z || !out) return fail(SSM_E_INVALID_ARG, "gate: NULL input or output");
+  const size_t es = io_size(io_dtype);
+  if (!aligned(y, es) || !aligned(z, es) || !aligned(out, es) || !aligned(d_norm_w, 4))
+    return fail(SSM_E_INVALID_ARG, "gate: misaligned pointer");
+  HIP_TRY(launch_gate(io_dtype, rows, C, group, y, z, d_norm_w, eps, out, as_stream(stream)));
   return SSM_OK;
 }
 

@@ -177,4 +177,33 @@ hipError_t launch_zero_u64(unsigned long long *p, int n, hipStream_t s);
 hipError_t launch_finite_check(int io, const void *p, size_t n, unsigned int *flag,
                                hipStream_t s);
 
+// ------------------------------------------------- conv1d and gated output
+// Causal depthwise conv over the token axis (width K <= kMaxConvK) with the
+// carried conv state [C, K-1] (the K-1 previous inputs, oldest first).
+constexpr int kMaxConvK = 4;
+constexpr int kConvResetsPerLaunch = 32;
+struct ConvChunkMeta {
+  int32_t n_rst;                       // resets inside [t_begin, t_end)
+  int32_t rst[kConvResetsPerLaunch];   // their token indices, ascending
+  int32_t first_before;                // latest reset before t_begin; -K: none (state visible)
+};
+struct ConvArgs {
+  const void *x;          // chunk: [L, C]; decode: [batch, C] (io dtype)
+  void *y;                // same layout
+  float *state;           // chunk: the slot's [C, K-1]; decode: every slot's [S, C, K-1]
+  const float *w, *bias;  // [C, K], [C] or null
+  int C, K, act;          // act: 1 = SiLU
+  int t_begin, t_end;     // chunk: the token range of this launch
+  int n;                  // decode: entries in this launch
+};
+hipError_t launch_conv_chunk(int io, const ConvArgs &a, const ConvChunkMeta &m, hipStream_t s);
+// after every launch of a chunk: the state becomes the last K-1 inputs
+// (first_final: latest reset in the chunk, or -K)
+hipError_t launch_conv_state(int io, const ConvArgs &a, int L, int first_final, hipStream_t s);
+hipError_t launch_conv_decode(int io, const ConvArgs &a, const DecodeMeta &m, hipStream_t s);
+// y * SiLU(z), then (norm_w non-null) each group of `group` channels divided
+// by its root mean square and scaled by norm_w
+hipError_t launch_gate(int io, int64_t rows, int C, int group, const void *y, const void *z,
+                       const float *norm_w, float eps, void *out, hipStream_t s);
+
 }  // namespace ssm

@@ -118,6 +118,11 @@ _SIGS = {
     "ssm_blob_bytes": [ctypes.POINTER(LayerDesc)],
     "ssm_state_serialize": [_H, _I32, _V, _SZ, ctypes.POINTER(_SZ), ctypes.POINTER(Receipt), _V],
     "ssm_state_deserialize": [_H, _I32, _V, _SZ, ctypes.POINTER(Receipt), _V],
+    "ssm_conv_state_bytes": [_I32, _I32, _I32],
+    "ssm_conv_attach": [_H, _I32, _I32, _I32, _V, _V, _V],
+    "ssm_conv_chunk": [_H, _I32, _I64, _V, _V, _V, _V],
+    "ssm_conv_decode": [_H, _I32, _V, _V, _V, _V, _V],
+    "ssm_gate": [_I32, _I64, _I32, _I32, _V, _V, _V, ctypes.c_float, _V, _V],
     "ssm_get_position": [_H, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_U64)],
     "ssm_get_log_state": [_H, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)],
     "ssm_get_counters": [_H, ctypes.POINTER(Counters)],
@@ -193,6 +198,28 @@ def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def conv_state_bytes(n_slots, C, K):
+    return int(_lib.ssm_conv_state_bytes(n_slots, C, K))
+
+
+def gate(y, z, norm_w=None, group=None, eps=1e-6, out=None, stream=None):
+    """out = y * SiLU(z) over [rows, C] (fp32 or bf16 device tensors); with
+    norm_w [C] fp32, each group of `group` channels is RMS-normalised."""
+    torch = _torch()
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("gate: y must be float32 or bfloat16")
+    io = SSM_BF16 if y.dtype == torch.bfloat16 else SSM_F32
+    rows, C = y.shape
+    group = C if group is None else group
+    if out is None:
+        out = torch.empty_like(y)
+    _check(_lib.ssm_gate(io, rows, C, group, _dev_ptr(y, y.dtype, (rows, C), "y"),
+                         _dev_ptr(z, y.dtype, (rows, C), "z"),
+                         None if norm_w is None else _dev_ptr(norm_w, torch.float32, (C,), "norm_w"),
+                         float(eps), _dev_ptr(out, y.dtype, (rows, C), "out"), _stream(stream)))
+    return out
 
 
 class StreamState:
@@ -413,6 +440,50 @@ class StreamState:
         r = Receipt.from_dict(receipt)
         _check(_lib.ssm_state_deserialize(self.handle, int(slot), blob, len(blob),
                                           ctypes.byref(r), _stream(stream)))
+
+    # ------------------------------------------------------ conv1d (before the scan)
+    def conv_attach(self, C, K, w, bias=None, act=True, state=None):
+        """Causal depthwise conv of C channels and width K: w [C, K] and bias
+        [C] fp32 device tensors; the conv state [S, C, K-1] fp32 (zeroed here
+        when allocated)."""
+        torch = _torch()
+        if state is None and K > 1:
+            state = torch.zeros((self.S, C, K - 1), dtype=torch.float32,
+                                device=self.state.device)
+        _check(_lib.ssm_conv_attach(
+            self.handle, int(C), int(K), 1 if act else 0,
+            None if K == 1 else _dev_ptr(state, torch.float32, (self.S, C, K - 1), "conv state"),
+            _dev_ptr(w, torch.float32, (C, K), "w"),
+            None if bias is None else _dev_ptr(bias, torch.float32, (C,), "bias")))
+        self.conv_C, self.conv_K, self.conv_w, self.conv_b = C, K, w, bias
+        self.conv_state = state
+
+    def conv_chunk(self, slot, x, reset=None, y=None, stream=None):
+        torch = _torch()
+        L = x.shape[0]
+        if y is None:
+            y = torch.empty((L, self.conv_C), dtype=self.io_dtype, device=x.device)
+        rs, rp = _host(reset, np.uint8)
+        if rs is not None and len(rs) != L:
+            raise ValueError("reset must have one flag per token")
+        _check(_lib.ssm_conv_chunk(self.handle, int(slot), L,
+                                   _dev_ptr(x, self.io_dtype, (L, self.conv_C), "x"), rp,
+                                   _dev_ptr(y, self.io_dtype, (L, self.conv_C), "y"),
+                                   _stream(stream)))
+        return y
+
+    def conv_decode(self, slot_ids, x, reset=None, y=None, stream=None):
+        torch = _torch()
+        ids, ip = _host(slot_ids, np.int32)
+        b = len(ids)
+        if y is None:
+            y = torch.empty((b, self.conv_C), dtype=self.io_dtype, device=x.device)
+        rs, rp = _host(reset, np.uint8)
+        _check(_lib.ssm_conv_decode(self.handle, b, ip,
+                                    _dev_ptr(x, self.io_dtype, (b, self.conv_C), "x"), rp,
+                                    _dev_ptr(y, self.io_dtype, (b, self.conv_C), "y"),
+                                    _stream(stream)))
+        return y
 
     def position(self, slot):
         p, c = _I64(0), _U64(0)

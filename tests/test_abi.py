@@ -238,3 +238,34 @@ def test_deserialize_rejects_before_any_device_work():
     assert lib.ssm_state_deserialize(h, 1, None, 0, ctypes.byref(r),
                                      None) == ssm.SSM_E_INVALID_ARG
     lib.ssm_destroy(h)
+
+
+def test_conv_and_gate_argument_checks():
+    lib = ssm.lib()
+    assert lib.ssm_conv_state_bytes(4, 10, 4) == 4 * 10 * 3 * 4
+    assert lib.ssm_conv_state_bytes(4, 10, 5) == 0 and lib.ssm_conv_state_bytes(4, 0, 4) == 0
+    rc, h = _create(desc=_desc())
+    # no conv attached yet
+    assert lib.ssm_conv_chunk(h, 0, 8, FAKE, None, FAKE, None) == ssm.SSM_E_INVALID_STATE
+    assert lib.ssm_conv_decode(h, 1, (ctypes.c_int32 * 1)(0), FAKE, None, FAKE,
+                               None) == ssm.SSM_E_INVALID_STATE
+    for C, K, act in ((0, 4, 1), (8, 0, 1), (8, 5, 1), (8, 4, 2)):
+        assert lib.ssm_conv_attach(h, C, K, act, FAKE, FAKE, None) == ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_conv_attach(h, 8, 4, 1, None, FAKE, None) == ssm.SSM_E_INVALID_ARG  # no state
+    assert lib.ssm_conv_attach(h, 8, 4, 1, FAKE, FAKE, None) == ssm.SSM_OK
+    assert lib.ssm_conv_chunk(h, 9, 8, FAKE, None, FAKE, None) == ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_conv_chunk(h, 0, -1, FAKE, None, FAKE, None) == ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_conv_chunk(h, 0, 0, None, None, None, None) == ssm.SSM_OK  # empty chunk
+    # y overlapping x is refused (the window reads inputs other threads overwrite)
+    x = ctypes.c_void_p(0x10000)
+    y = ctypes.c_void_p(0x10000 + 4 * 8 * 3)
+    assert lib.ssm_conv_chunk(h, 0, 8, x, None, y, None) == ssm.SSM_E_INVALID_ARG
+    assert "overlap" in _err()
+    dup = (ctypes.c_int32 * 2)(1, 1)
+    assert lib.ssm_conv_decode(h, 2, dup, FAKE, None, FAKE, None) == ssm.SSM_E_INVALID_ARG
+    lib.ssm_destroy(h)
+    gate = lib.ssm_gate
+    assert gate(ssm.SSM_F16, 4, 8, 8, FAKE, FAKE, None, 0.0, FAKE, None) == ssm.SSM_E_INVALID_ARG
+    assert gate(ssm.SSM_F32, 4, 8, 3, FAKE, FAKE, FAKE, 1e-6, FAKE, None) == ssm.SSM_E_INVALID_ARG
+    assert gate(ssm.SSM_F32, 4, 8, 4, FAKE, FAKE, FAKE, -1.0, FAKE, None) == ssm.SSM_E_INVALID_ARG
+    assert gate(ssm.SSM_F32, 0, 8, 8, None, None, None, 0.0, None, None) == ssm.SSM_OK
