@@ -42,78 +42,169 @@ template <typename T> struct Vec<T, 4> {
   }
 };
 
+template <> struct Vec<bf16_t, 8> {
+  static __device__ __forceinline__ void ld(const bf16_t *p, float *v) {
+    const uint4 r = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void st(bf16_t *p, const float *v) {
+    uint4 r;
+    r.x = pack2_bf16(v[0], v[1]);
+    r.y = pack2_bf16(v[2], v[3]);
+    r.z = pack2_bf16(v[4], v[5]);
+    r.w = pack2_bf16(v[6], v[7]);
+#if SSM_CONV_NT
+    __builtin_nontemporal_store(r.x, reinterpret_cast<uint32_t *>(p));
+    __builtin_nontemporal_store(r.y, reinterpret_cast<uint32_t *>(p) + 1);
+    __builtin_nontemporal_store(r.z, reinterpret_cast<uint32_t *>(p) + 2);
+    __builtin_nontemporal_store(r.w, reinterpret_cast<uint32_t *>(p) + 3);
+#else
+    *reinterpret_cast<uint4 *>(p) = r;
+#endif
+  }
+};
+
+// Raw V-element vectors (bf16 stays packed in registers until used).
+template <typename T, int V> struct Raw;
+template <> struct Raw<float, 4> {
+  typedef float4 type;
+  static __device__ __forceinline__ type ld(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+  static __device__ __forceinline__ float get(const type &r, int v) {
+    return v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w;
+  }
+  static __device__ __forceinline__ type zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+template <> struct Raw<bf16_t, 4> {
+  typedef uint2 type;
+  static __device__ __forceinline__ type ld(const bf16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+  static __device__ __forceinline__ float get(const type &r, int v) {
+    const uint32_t w = v < 2 ? r.x : r.y;
+    return __uint_as_float((v & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  static __device__ __forceinline__ type zero() { return make_uint2(0u, 0u); }
+};
+template <> struct Raw<bf16_t, 8> {
+  typedef uint4 type;
+  static __device__ __forceinline__ type ld(const bf16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+  static __device__ __forceinline__ float get(const type &r, int v) {
+    const uint32_t w = v < 2 ? r.x : v < 4 ? r.y : v < 6 ? r.z : r.w;
+    return __uint_as_float((v & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  static __device__ __forceinline__ type zero() { return make_uint4(0u, 0u, 0u, 0u); }
+};
+template <typename T> struct Raw<T, 1> {
+  typedef T type;
+  static __device__ __forceinline__ type ld(const T *p) { return *p; }
+  static __device__ __forceinline__ float get(const type &r, int) { return to_f(r); }
+  static __device__ __forceinline__ type zero() { return T{}; }
+};
 // Tokens per thread in the chunk kernel: all of a thread's inputs (its tokens
 // and the K-1 before them) are loaded before any output is stored.
-constexpr int kConvRun = 8;
+#ifndef SSM_CONV_RUN
+#define SSM_CONV_RUN 16
+#endif
+#ifndef SSM_CONV_NT
+#define SSM_CONV_NT 0
+#endif
+#ifndef SSM_CONV_V8
+#define SSM_CONV_V8 0
+#endif
+constexpr int kConvRun = SSM_CONV_RUN;
 
-// Grid (channel groups of kThreads * V, token runs of kConvRun).
+// Grid (channel groups of blockDim.x * V, token runs of kConvRun).  The K-1
+// window entries before the run are held as fp32 (they may come from the
+// carried state), the run's own inputs as raw io vectors (bf16 stays packed).
+// A run is "clean" when it is whole, has no reset inside and its window needs
+// neither the carried state nor a zeroed entry: the common case takes a copy
+// of the code without predicates.  Otherwise a reset at run position r zeroes
+// the entries of the tokens before it; every index into the register arrays
+// is a compile-time constant, so they stay in registers.
 template <typename T, int K, int V>
 __global__ __launch_bounds__(kThreads) void conv_chunk_kernel(ConvArgs a, ConvChunkMeta m) {
-  const int c0 = (blockIdx.x * kThreads + threadIdx.x) * V;
+  typedef Raw<T, V> R;
+  const int c0 = (blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (c0 >= a.C) return;
   const int C = a.C;
   const int t0 = a.t_begin + blockIdx.y * kConvRun;
   const int n = min(kConvRun, a.t_end - t0);
   const T *x = (const T *)a.x + c0;
   T *y = (T *)a.y + c0;
+  constexpr int KW = K - 1;
 
   // latest reset at or before t0 (resets are uniform: kernel arguments)
   int first = m.first_before, ri = 0;
   while (ri < m.n_rst && m.rst[ri] <= t0) first = m.rst[ri++];
+  const bool clean = n == kConvRun && t0 - KW >= max(first, 0) &&
+                     (ri >= m.n_rst || m.rst[ri] >= t0 + kConvRun);
 
-  // inputs: tokens t0 - (K-1) .. t0 + n - 1 (the window, then the run)
-  constexpr int KW = K - 1;
-  float in[KW + kConvRun][V];
-#pragma unroll
-  for (int j = 0; j < KW; ++j) {
-    const int src = t0 - KW + j;
-    if (src >= first && src >= 0) {
-      Vec<T, V>::ld(x + (size_t)src * C, in[j]);
-    } else {
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        in[j][v] = (src >= first) ? a.state[(size_t)(c0 + v) * KW + (src + KW)] : 0.f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kConvRun; ++i) {
-    if (i < n) {
-      Vec<T, V>::ld(x + (size_t)(t0 + i) * C, in[KW + i]);
-    } else {
-#pragma unroll
-      for (int v = 0; v < V; ++v) in[KW + i][v] = 0.f;
-    }
-  }
+  float win[KW > 0 ? KW : 1][V];
+  typename R::type run[kConvRun];
   float w[K][V], b[V];
+  // entry j of the combined window + run, channel v
+  auto in = [&](int j, int v) { return j < KW ? win[j][v] : R::get(run[j - KW], v); };
+  auto emit = [&](int i) {
+    float out[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float acc = b[v];
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc += w[k][v] * in(i + k, v);
+      out[v] = a.act ? silu(acc) : acc;
+    }
+    Vec<T, V>::st(y + (size_t)(t0 + i) * C, out);
+  };
+  if (clean) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) Vec<T, V>::ld(x + (size_t)(t0 - KW + j) * C, win[j]);
+#pragma unroll
+    for (int i = 0; i < kConvRun; ++i) run[i] = R::ld(x + (size_t)(t0 + i) * C);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const int src = t0 - KW + j;
+      if (src >= first && src >= 0) {
+        Vec<T, V>::ld(x + (size_t)src * C, win[j]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          win[j][v] = (src >= first) ? a.state[(size_t)(c0 + v) * KW + (src + KW)] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kConvRun; ++i) run[i] = i < n ? R::ld(x + (size_t)(t0 + i) * C) : R::zero();
+  }
 #pragma unroll
   for (int v = 0; v < V; ++v) {
 #pragma unroll
     for (int k = 0; k < K; ++k) w[k][v] = a.w[(size_t)(c0 + v) * K + k];
     b[v] = a.bias ? a.bias[c0 + v] : 0.f;
   }
-
-  // a reset at token t0 + i hides window entries before it
-  int rlast = -1;  // run-relative index of the latest reset seen inside the run
+  if (clean) {
+#pragma unroll
+    for (int i = 0; i < kConvRun; ++i) emit(i);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kConvRun; ++i) {
     if (i < n) {
-      if (ri < m.n_rst && m.rst[ri] == t0 + i) {
-        rlast = i;
+      if (ri < m.n_rst && m.rst[ri] == t0 + i) {  // hide the inputs before token t0 + i
         ++ri;
-      }
-      float out[V];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        float acc = b[v];
+        for (int j = i; j < i + KW; ++j) {
+          if (j < KW) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const int j = i + k;  // index into in[]: token t0 + i - (K-1) + k
-          const bool vis = rlast < 0 || j - KW >= rlast;
-          acc += vis ? w[k][v] * in[j][v] : 0.f;
+            for (int v = 0; v < V; ++v) win[j][v] = 0.f;
+          } else {
+            run[j - KW] = R::zero();
+          }
         }
-        out[v] = a.act ? silu(acc) : acc;
       }
-      Vec<T, V>::st(y + (size_t)(t0 + i) * C, out);
+      emit(i);
     }
   }
 }
@@ -181,10 +272,25 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(const T *y, const T *z, 
   Vec<T, V>::st(out + i, o);
 }
 
-// Gated group RMS norm: one workgroup per (row, group).  Pass 1 sums the
-// squares of g = y * SiLU(z) over the group; pass 2 recomputes g (the group's
-// inputs are still in L2) and writes g / rms * w.
-constexpr int kGateU = 4;  // vectors in flight per thread and pass
+// Gated group RMS norm: one workgroup per (row, group).  g = y * SiLU(z) is
+// computed once and kept in registers (kGateRegs vectors per thread) while
+// the group's sum of squares is reduced; groups larger than that take two
+// passes, recomputing g from y and z (still in L2) in the second.
+#ifndef SSM_GATE_REGS
+#define SSM_GATE_REGS 8
+#endif
+constexpr int kGateRegs = SSM_GATE_REGS;
+
+__device__ __forceinline__ float block_sum(float v, float *part) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) tot += part[i];
+  return tot;
+}
 
 template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void gate_norm_kernel(const T *y, const T *z,
@@ -194,11 +300,52 @@ __global__ __launch_bounds__(kThreads) void gate_norm_kernel(const T *y, const T
   const size_t base = (size_t)blockIdx.x * C + (size_t)blockIdx.y * group;
   const float *wg = w + (size_t)blockIdx.y * group;
   const int nv = group / V;  // vectors in the group
-  float ss = 0.f;
-  for (int i0 = threadIdx.x; i0 < nv; i0 += kThreads * kGateU) {
-    float yv[kGateU][V], zv[kGateU][V];
+  if (nv <= kThreads * kGateRegs) {
+    float g[kGateRegs][V];
+    float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < kGateU; ++u) {
+    for (int u = 0; u < kGateRegs; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      float yv[V], zv[V];
+      if (i < nv) {
+        Vec<T, V>::ld(y + base + (size_t)i * V, yv);
+        Vec<T, V>::ld(z + base + (size_t)i * V, zv);
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) yv[v] = zv[v] = 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        g[u][v] = yv[v] * silu(zv[v]);
+        ss += g[u][v] * g[u][v];
+      }
+    }
+    const float inv = rsqrtf(block_sum(ss, part) / (float)group + eps);
+    // the weights (shared by every row, so L2 hits) are loaded before any store
+    float wv[kGateRegs][V];
+#pragma unroll
+    for (int u = 0; u < kGateRegs; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      if (i < nv) Vec<float, V>::ld(wg + (size_t)i * V, wv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kGateRegs; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      if (i < nv) {
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = g[u][v] * inv * wv[u][v];
+        Vec<T, V>::st(out + base + (size_t)i * V, o);
+      }
+    }
+    return;
+  }
+  constexpr int U = 4;
+  float ss = 0.f;
+  for (int i0 = threadIdx.x; i0 < nv; i0 += kThreads * U) {
+    float yv[U][V], zv[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const int i = i0 + u * kThreads;
       if (i < nv) {
         Vec<T, V>::ld(y + base + (size_t)i * V, yv[u]);
@@ -209,25 +356,18 @@ __global__ __launch_bounds__(kThreads) void gate_norm_kernel(const T *y, const T
       }
     }
 #pragma unroll
-    for (int u = 0; u < kGateU; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const float g = yv[u][v] * silu(zv[u][v]);
-        ss += g * g;
+        const float gv = yv[u][v] * silu(zv[u][v]);
+        ss += gv * gv;
       }
   }
+  const float inv = rsqrtf(block_sum(ss, part) / (float)group + eps);
+  for (int i0 = threadIdx.x; i0 < nv; i0 += kThreads * U) {
+    float yv[U][V], zv[U][V], wv[U][V];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) tot += part[i];
-  const float inv = rsqrtf(tot / (float)group + eps);
-  for (int i0 = threadIdx.x; i0 < nv; i0 += kThreads * kGateU) {
-    float yv[kGateU][V], zv[kGateU][V], wv[kGateU][V];
-#pragma unroll
-    for (int u = 0; u < kGateU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i = i0 + u * kThreads;
       if (i < nv) {
         Vec<T, V>::ld(y + base + (size_t)i * V, yv[u]);
@@ -236,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void gate_norm_kernel(const T *y, const T
       }
     }
 #pragma unroll
-    for (int u = 0; u < kGateU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i = i0 + u * kThreads;
       if (i < nv) {
         float o[V];
@@ -248,16 +388,34 @@ __global__ __launch_bounds__(kThreads) void gate_norm_kernel(const T *y, const T
   }
 }
 
+// Threads per block (a multiple of 64, at most kThreads) that leaves the
+// fewest idle threads over `units` channel vectors.
+static int fit_block(int units) {
+  int best = kThreads, waste = (units + kThreads - 1) / kThreads * kThreads - units;
+  for (int b = kThreads - 64; b >= 64; b -= 64) {
+    const int w = (units + b - 1) / b * b - units;
+    if (w < waste) best = b, waste = w;
+  }
+  return best;
+}
+
 template <typename T, int K>
 hipError_t conv_chunk_k(const ConvArgs &a, const ConvChunkMeta &m, hipStream_t s) {
   const int runs = (a.t_end - a.t_begin + kConvRun - 1) / kConvRun;
   const bool v4 = a.C % 4 == 0 && ((((uintptr_t)a.x | (uintptr_t)a.y) & (4 * sizeof(T) - 1)) == 0);
-  if (v4) {
-    dim3 grid((a.C / 4 + kThreads - 1) / kThreads, runs);
-    hipLaunchKernelGGL((conv_chunk_kernel<T, K, 4>), grid, dim3(kThreads), 0, s, a, m);
+  const bool v8 = sizeof(T) == 2 && a.C % 8 == 0 && ((((uintptr_t)a.x | (uintptr_t)a.y) & 15) == 0);
+  if (SSM_CONV_V8 && v8) {
+    const int b = fit_block(a.C / 8);
+    dim3 grid((a.C / 8 + b - 1) / b, runs);
+    hipLaunchKernelGGL((conv_chunk_kernel<bf16_t, K, 8>), grid, dim3(b), 0, s, a, m);
+  } else if (v4) {
+    const int b = fit_block(a.C / 4);
+    dim3 grid((a.C / 4 + b - 1) / b, runs);
+    hipLaunchKernelGGL((conv_chunk_kernel<T, K, 4>), grid, dim3(b), 0, s, a, m);
   } else {
-    dim3 grid((a.C + kThreads - 1) / kThreads, runs);
-    hipLaunchKernelGGL((conv_chunk_kernel<T, K, 1>), grid, dim3(kThreads), 0, s, a, m);
+    const int b = fit_block(a.C);
+    dim3 grid((a.C + b - 1) / b, runs);
+    hipLaunchKernelGGL((conv_chunk_kernel<T, K, 1>), grid, dim3(b), 0, s, a, m);
   }
   return hipGetLastError();
 }
