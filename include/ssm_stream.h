@@ -284,21 +284,30 @@ ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
  * raw element bytes, all little-endian. */
 size_t ssm_blob_bytes(const ssm_layer_desc *desc);
 
-/* Checkpoint `slot` into a host blob: materialize it, write one fp32 array of
- * shape [H, P, N] (dtype code 0) into h_blob (caller-owned host memory of
- * `cap` bytes; SSM_E_INVALID_ARG if cap < ssm_blob_bytes), set *written and
- * fill *out as ssm_state_checkpoint does.  The blob carries only the state;
- * the receipt travels beside it.  Synchronises `stream`. */
+/* Bytes of the blob ssm_state_serialize writes for a slot of this handle:
+ * ssm_blob_bytes, plus 16 + 4*C*(K-1) when a conv of width K > 1 is attached
+ * (ssm_conv_attach); 0 for a handle that is not live. */
+size_t ssm_state_blob_bytes(ssm_handle h);
+
+/* Checkpoint `slot` into a host blob: materialize it and write the slot's
+ * state as fp32 arrays (dtype code 0) into h_blob (caller-owned host memory of
+ * `cap` bytes; SSM_E_INVALID_ARG if cap < ssm_state_blob_bytes): the conv
+ * state [C, K-1] first when a conv with K > 1 is attached, then the scan
+ * state [H, P, N] (a Mamba layer's [conv_state, ssm_state]).  Sets *written
+ * and fills *out as ssm_state_checkpoint does (its checksum covers the scan
+ * state).  The receipt travels beside the blob.  Synchronises `stream`. */
 ssm_status ssm_state_serialize(ssm_handle h, int32_t slot, void *h_blob, size_t cap,
                                size_t *written, ssm_receipt *out, void *stream);
 
 /* Resume `slot` from a host blob of `len` bytes and its receipt (the
  * section "Make reset, checkpoint, and cancellation observable" of "Mamba
  * Streaming State That Survives Chunking": a resume that does not match is
- * refused).  The blob may hold several arrays; the state is the last one
+ * refused).  The blob may hold several arrays; the scan state is the last one
  * (a Mamba blob is [conv_state, ssm_state]), of shape [H, P, N] after any
- * leading extents of 1, with dtype code 0 or 2 (fp32 words; for code 2 every
- * word must be a bf16 value) or 1 (fp16, widened exactly).  SSM_E_SCHEMA,
+ * leading extents of 1; with a conv of K > 1 attached the array before it is
+ * the conv state, [C, K-1] (required).  Dtype codes 0 or 2 (fp32 words; for
+ * code 2 every word must be a bf16 value) or 1 (fp16, widened exactly).
+ * SSM_E_SCHEMA,
  * with the slot unchanged, for a malformed blob (wrong version, truncated,
  * trailing bytes, unknown dtype code), a state array of the wrong shape, a
  * receipt that does not match the handle, or a checksum (taken over the

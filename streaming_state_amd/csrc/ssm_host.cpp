@@ -1038,7 +1038,46 @@ static const char *parse_blob(const uint8_t *p, size_t len, std::vector<BlobArra
   return nullptr;
 }
 
+// Decode array `a` into fp32 words if its extents are `want` after any
+// leading extents of 1; nullptr on success, else what is wrong.
+static const char *decode_array(const BlobArray &a, std::initializer_list<uint32_t> want,
+                                const char *wrong_shape, std::vector<float> *out) {
+  const size_t rank = a.shape.size(), nw = want.size();
+  if (rank < nw) return wrong_shape;
+  size_t k = 0;
+  for (; k + nw < rank; ++k)
+    if (a.shape[k] != 1) return wrong_shape;
+  for (uint32_t e : want)
+    if (a.shape[k++] != e) return wrong_shape;
+  out->resize(a.count);
+  if (a.dtype == kBlobF16) {
+    for (size_t i = 0; i < a.count; ++i)
+      (*out)[i] = half_to_float((uint16_t)(a.data[2 * i] | a.data[2 * i + 1] << 8));
+  } else {
+    memcpy(out->data(), a.data, a.count * 4);
+    if (a.dtype == kBlobBF16)
+      for (size_t i = 0; i < a.count; ++i) {
+        uint32_t w;
+        memcpy(&w, &(*out)[i], 4);
+        if (w & 0xffffu) return "bf16 array holds a value bf16 cannot represent";
+      }
+  }
+  return nullptr;
+}
+
+// Blob of a handle's slot: [conv_state [C, K-1], ssm_state [H, P, N]] with a
+// conv of K > 1 attached (a Mamba layer's pair), else [ssm_state].
+static size_t conv_blob_part(const Handle *H) {
+  return H->conv_floats() ? 4 + 2 * 4 + 4 + H->conv_floats() * sizeof(float) : 0;
+}
+static size_t handle_blob_size(const Handle *H) { return blob_size(H->d) + conv_blob_part(H); }
+
 }  // namespace
+
+size_t ssm_state_blob_bytes(ssm_handle h) {
+  Handle *H = lookup(h);
+  return H ? handle_blob_size(H) : 0;
+}
 
 size_t ssm_blob_bytes(const ssm_layer_desc *desc) {
   if (check_desc(desc) != SSM_OK) return 0;
@@ -1051,7 +1090,7 @@ ssm_status ssm_state_serialize(ssm_handle h, int32_t slot, void *h_blob, size_t 
   if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "serialize: bad slot %d", slot);
   if (!h_blob || !written || !out)
     return fail(SSM_E_INVALID_ARG, "serialize: NULL blob, length or receipt pointer");
-  const size_t need = blob_size(H->d);
+  const size_t need = handle_blob_size(H);
   if (cap < need)
     return fail(SSM_E_INVALID_ARG, "serialize: blob capacity %zu below the %zu bytes needed", cap,
                 need);
@@ -1062,16 +1101,27 @@ ssm_status ssm_state_serialize(ssm_handle h, int32_t slot, void *h_blob, size_t 
   ssm_status st = materialize(H, 1, &one, s);
   if (st != SSM_OK) return st;
   // Bounce through an aligned host buffer: the payload sits 28 bytes into the blob.
-  const size_t nf = H->state_bytes() / 4;
-  std::vector<float> host(nf);
+  const size_t nf = H->state_bytes() / 4, nc = H->conv_floats();
+  std::vector<float> host(nf), conv(nc);
   HIP_TRY(hipMemcpyAsync(host.data(), H->slot_state(slot), H->state_bytes(),
                          hipMemcpyDeviceToHost, s));
+  if (nc)
+    HIP_TRY(hipMemcpyAsync(conv.data(), H->conv_state + (size_t)slot * nc, nc * sizeof(float),
+                           hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
   uint8_t *b = static_cast<uint8_t *>(h_blob);
-  const uint32_t head[7] = {kBlobVersion, 1u, 3u, (uint32_t)H->d.H, (uint32_t)H->d.P,
-                            (uint32_t)H->d.N, kBlobF32};
-  for (int i = 0; i < 7; ++i) put_u32(b + 4 * i, head[i]);
-  memcpy(b + 28, host.data(), H->state_bytes());
+  put_u32(b, kBlobVersion);
+  put_u32(b + 4, nc ? 2u : 1u);
+  uint8_t *p = b + 8;
+  if (nc) {
+    const uint32_t ch[4] = {2u, (uint32_t)H->conv_C, (uint32_t)(H->conv_K - 1), kBlobF32};
+    for (int i = 0; i < 4; ++i) put_u32(p + 4 * i, ch[i]);
+    memcpy(p + 16, conv.data(), nc * sizeof(float));
+    p += 16 + nc * sizeof(float);
+  }
+  const uint32_t head[5] = {3u, (uint32_t)H->d.H, (uint32_t)H->d.P, (uint32_t)H->d.N, kBlobF32};
+  for (int i = 0; i < 5; ++i) put_u32(p + 4 * i, head[i]);
+  memcpy(p + 20, host.data(), H->state_bytes());
   *written = need;
   const Slot &sl = H->slots[slot];
   ssm_receipt r{};
@@ -1111,27 +1161,21 @@ ssm_status ssm_state_deserialize(ssm_handle h, int32_t slot, const void *h_blob,
   std::vector<BlobArray> arrays;
   if (const char *bad = parse_blob(static_cast<const uint8_t *>(h_blob), len, &arrays))
     return reject(bad);
-  // The recurrent state is the last array (a Mamba blob is [conv_state, ssm_state]);
-  // its extents are [H, P, N], optionally after leading extents of 1.
-  const BlobArray &a = arrays.back();
-  const size_t rank = a.shape.size();
-  bool shape_ok = rank >= 3 && a.shape[rank - 3] == (uint32_t)H->d.H &&
-                  a.shape[rank - 2] == (uint32_t)H->d.P && a.shape[rank - 1] == (uint32_t)H->d.N;
-  for (size_t k = 0; shape_ok && k + 3 < rank; ++k) shape_ok = a.shape[k] == 1;
-  if (!shape_ok) return reject("state array is not [H, P, N] for this handle");
-  const size_t nf = a.count;
-  std::vector<float> host(nf);
-  if (a.dtype == kBlobF16) {
-    for (size_t i = 0; i < nf; ++i)
-      host[i] = half_to_float((uint16_t)(a.data[2 * i] | a.data[2 * i + 1] << 8));
-  } else {
-    memcpy(host.data(), a.data, nf * 4);
-    if (a.dtype == kBlobBF16)
-      for (size_t i = 0; i < nf; ++i) {
-        uint32_t w;
-        memcpy(&w, &host[i], 4);
-        if (w & 0xffffu) return reject("bf16 array holds a value bf16 cannot represent");
-      }
+  // The recurrent state is the last array, [H, P, N] after any leading
+  // extents of 1.  With a conv attached the one before it is the conv state,
+  // [C, K-1] (a Mamba blob is [conv_state, ssm_state]).
+  std::vector<float> host, conv;
+  if (const char *bad = decode_array(arrays.back(),
+                                     {(uint32_t)H->d.H, (uint32_t)H->d.P, (uint32_t)H->d.N},
+                                     "state array is not [H, P, N] for this handle", &host))
+    return reject(bad);
+  const size_t nf = host.size(), nc = H->conv_floats();
+  if (nc) {
+    if (arrays.size() < 2) return reject("lacks the conv state this handle carries");
+    if (const char *bad = decode_array(arrays[arrays.size() - 2],
+                                       {(uint32_t)H->conv_C, (uint32_t)(H->conv_K - 1)},
+                                       "conv state array is not [C, K-1] for this handle", &conv))
+      return reject(bad);
   }
   if (host_checksum(host.data(), nf) != r->checksum) {
     H->cnt.restores_rejected++;
@@ -1140,6 +1184,9 @@ ssm_status ssm_state_deserialize(ssm_handle h, int32_t slot, const void *h_blob,
   hipStream_t s = as_stream(stream);
   HIP_TRY(hipMemcpyAsync(H->slot_state(slot), host.data(), H->state_bytes(),
                          hipMemcpyHostToDevice, s));
+  if (nc)
+    HIP_TRY(hipMemcpyAsync(H->conv_state + (size_t)slot * nc, conv.data(), nc * sizeof(float),
+                           hipMemcpyHostToDevice, s));
   HIP_TRY(hipStreamSynchronize(s));
   adopt_receipt(H, slot, r);
   return SSM_OK;

@@ -116,6 +116,7 @@ _SIGS = {
     "ssm_state_checkpoint": [_H, _I32, _V, ctypes.POINTER(Receipt), _V],
     "ssm_state_restore": [_H, _I32, _V, ctypes.POINTER(Receipt), _V],
     "ssm_blob_bytes": [ctypes.POINTER(LayerDesc)],
+    "ssm_state_blob_bytes": [_H],
     "ssm_state_serialize": [_H, _I32, _V, _SZ, ctypes.POINTER(_SZ), ctypes.POINTER(Receipt), _V],
     "ssm_state_deserialize": [_H, _I32, _V, _SZ, ctypes.POINTER(Receipt), _V],
     "ssm_conv_state_bytes": [_I32, _I32, _I32],
@@ -424,7 +425,7 @@ class StreamState:
                                       ctypes.byref(r), _stream(stream)))
 
     def blob_bytes(self):
-        return int(_lib.ssm_blob_bytes(ctypes.byref(self.desc)))
+        return int(_lib.ssm_state_blob_bytes(self.handle))
 
     def serialize(self, slot, stream=None):
         """The slot's state as a state blob (bytes) and its receipt."""

@@ -162,3 +162,52 @@ def test_rejected_blob_leaves_slot_untouched(ssm):
     assert torch.equal(before, h.state[1]) and h.position(1) == pos
     assert h.counters()["restores_rejected"] == 3
     h.destroy()
+
+
+def test_mamba_pair_blob_with_conv_state(ssm):
+    """With the conv attached a slot's state is the pair [conv_state, ssm_state]
+    (the page's Mamba blob).  A layer step: the conv (SiLU) over the channels
+    [x | B | C], then the scan decode on its output.  Serialize after 48 steps,
+    hydrate another slot, continue both 48 more: bitwise equal."""
+    H, P, N, G, K = 4, 64, 128, 1, 4
+    Cc = H * P + 2 * G * N
+    say("mamba pair blob", dict(H=H, P=P, N=N, C=Cc, K=K))
+    h, A, D = _layer(ssm, 65, 2, H, P, N, schema_version=3, model_rev=5)
+    r = np.random.default_rng(65)
+    w = to_dev((r.standard_normal((Cc, K)) * 0.5).astype(np.float32))
+    b = to_dev((r.standard_normal(Cc) * 0.1).astype(np.float32))
+    h.conv_attach(Cc, K, w, b, act=True)
+    steps = 96
+    xbc = to_dev(r.standard_normal((steps, Cc)).astype(np.float32))
+    _, dt, _, _ = inputs.tokens(65, steps, H, P, N)
+    dtd = to_dev(dt)
+
+    def layer_step(slots, t):
+        n = len(slots)
+        u = h.conv_decode(slots, xbc[t:t + 1].expand(n, Cc).contiguous())
+        x = u[:, :H * P].reshape(n, H, P).contiguous()
+        Bm = u[:, H * P:H * P + G * N].reshape(n, G, N).contiguous()
+        Cm = u[:, H * P + G * N:].reshape(n, G, N).contiguous()
+        y = h.decode_step(slots, x, dtd[t:t + 1].expand(n, H).contiguous(), Bm, Cm)
+        return u, y
+
+    for t in range(48):
+        layer_step([0], t)
+    blob, rec = h.serialize(0)
+    assert len(blob) == h.blob_bytes() == 8 + 16 + Cc * (K - 1) * 4 + 20 + H * P * N * 4
+    arrays = oblob.read(blob)
+    assert [a.shape for _, a in arrays] == [(Cc, K - 1), (H, P, N)]
+    assert arrays[0][1].tobytes() == h.conv_state[0].cpu().numpy().tobytes()
+    assert arrays[1][1].tobytes() == h.state[0].cpu().numpy().tobytes()
+    # a blob without the conv state is refused by a handle that carries one
+    with pytest.raises(ssm.SSMError) as e:
+        h.deserialize(1, oblob.write([arrays[1]]), rec)
+    assert e.value.code == ssm.SSM_E_SCHEMA
+    h.deserialize(1, blob, rec)
+    outs = [layer_step([0, 1], t) for t in range(48, steps)]
+    torch.cuda.synchronize()
+    for u, y in outs:
+        assert torch.equal(u[0], u[1]) and torch.equal(y[0], y[1])
+    assert torch.equal(h.state[0], h.state[1])
+    assert torch.equal(h.conv_state[0], h.conv_state[1])
+    h.destroy()
