@@ -128,7 +128,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", default="", help="comma list of decode,replay,copy,prefill (profiling)")
+    ap.add_argument("--only", default="", help="comma list of decode,replay,copy,prefill,conv (profiling)")
     ap.add_argument("--skip-extras", action="store_true")
     return ap.parse_args()
 
@@ -352,6 +352,8 @@ def main():
 
     # ------------------------------------------------------------- extras
     extras = {}
+    if "conv" in only:  # the steps around the scan alone (for profiling)
+        extras["conv_and_gate"] = conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev)
     if not args.skip_extras and not only:
         # replay at W = 8 and 32 against the same copy baseline
         for W in (8, 32):
