@@ -48,12 +48,12 @@ DECODE_COUNTERS = {
 }
 
 
-# The same for scan_ssd_kernel on the 65,536-token prefill (mean per dispatch
+# The same for scan_ssd_pair_kernel on the 65,536-token prefill (mean per dispatch
 # over 4 dispatches): MFMA busy cycles summed over all SIMDs, GPU-active
 # cycles summed over the 8 XCDs, bf16 MFMA operations (x512 = flops), and the
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
-    "sources": ["ssm_ssd.hip", "ssm_device.h", "ssm_internal.h"],
+    "sources": ["ssm_ssd_pair.hip", "ssm_device.h", "ssm_internal.h"],
     "sha256": "dcb2361100bbed7cff246ff0d9b143e50bbf9312b6497ab9d9f7bb99f4601550",
     "mfma_busy_cycles": 420020224.0, "gui_active_cycles": 19655994.67, "xcds": 8, "simds": 1024,
     "mfma_mops_bf16": 840040448.0,
@@ -343,7 +343,7 @@ def main():
         comp["prefill"]["TFLOPs_algorithmic"] = tf
         pc = prefill_counters()
         comp["prefill"]["roofline"] = {
-            "bound": "mfma", "kernel": "scan_ssd_kernel", "achieved": round(tf, 1),
+            "bound": "mfma", "kernel": "scan_ssd_pair_kernel", "achieved": round(tf, 1),
             "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4),
             "mfma_busy_frac_counter": pc and pc["mfma_busy_frac"],
             "mfma_flops_executed": pc and pc["mfma_flops_executed"],

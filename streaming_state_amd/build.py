@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm_stream.so")
-SOURCES = ["ssm_host.cpp", "ssm_decode.hip", "ssm_kernels.hip", "ssm_scan.hip", "ssm_ssd.hip", "ssm_chunk.hip", "ssm_conv.hip"]
+SOURCES = ["ssm_host.cpp", "ssm_decode.hip", "ssm_kernels.hip", "ssm_scan.hip", "ssm_ssd.hip", "ssm_ssd_pair.hip", "ssm_chunk.hip", "ssm_conv.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

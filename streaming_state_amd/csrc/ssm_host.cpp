@@ -519,7 +519,9 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
     a.d = H->d;
     a.n_seg = ns;
     a.n_ck = nck;
-    if (ssd)
+    if (ssd && ssd_pair_supported(a))
+      HIP_TRY(launch_scan_ssd_pair(a, m, s));
+    else if (ssd)
       HIP_TRY(launch_scan_ssd(a, m, s));
     else
       HIP_TRY(launch_scan(H->io, a, m, s));

@@ -135,6 +135,10 @@ hipError_t launch_scan(int io, const ScanArgs &a, const ScanMeta &m, hipStream_t
 // 16-byte aligned).
 bool ssd_supported(int io, const Dims &d);
 hipError_t launch_scan_ssd(const ScanArgs &a, const ScanMeta &m, hipStream_t s);
+// The same form for a pair of heads per workgroup (heads 2i, 2i+1 share a B/C
+// group): H and H/G even, dt 4-byte aligned.
+bool ssd_pair_supported(const ScanArgs &a);
+hipError_t launch_scan_ssd_pair(const ScanArgs &a, const ScanMeta &m, hipStream_t s);
 
 // -------------------------------------------------- scan, tile-parallel form
 // Tiles of kChunkTile tokens; at most kChunkTilesPerLaunch tiles per launch

@@ -235,22 +235,6 @@ __device__ __forceinline__ void stage_load(Staged &st, const ScanArgs &a, int t0
   st.dt = dtg[(size_t)(t0 + min(lane, len - 1)) * d.H + h];
 }
 
-// Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 within each
-// 16-lane row, then row 15's and row 31's totals broadcast forward.
-__device__ __forceinline__ float scan64(float v) {
-  const int z = 0;
-#define SSD_SHR(ctrl, rmask)                                                               \
-  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), ctrl, rmask, 0xF, true))
-  SSD_SHR(0x111, 0xF);  // row_shr:1
-  SSD_SHR(0x112, 0xF);  // row_shr:2
-  SSD_SHR(0x114, 0xF);  // row_shr:4
-  SSD_SHR(0x118, 0xF);  // row_shr:8
-  SSD_SHR(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
-  SSD_SHR(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
-#undef SSD_SHR
-  return v;
-}
-
 __device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
   return ok ? v : make_uint4(0, 0, 0, 0);
 }

@@ -102,6 +102,12 @@ def test_workload1_streaming(ssm, chunk, ws):
     (4, 72, 128, 2, "f32", 130),
     (2, 64, 128, 1, "bf16", 301),
     (4, 16, 64, 4, "bf16", 77),
+    # the MFMA form: head pairs sharing a group, an odd head count (one head
+    # per workgroup), pairs over two groups, one head per group
+    (6, 64, 128, 1, "bf16", 203),
+    (3, 64, 128, 1, "bf16", 150),
+    (4, 64, 128, 2, "bf16", 200),
+    (4, 64, 128, 4, "bf16", 90),
 ])
 def test_ragged_resets_checkpoints(ssm, H, P, N, G, io, L):
     say("scan ragged", H, P, N, G, io, L)
