@@ -71,29 +71,28 @@ static_assert(kSmemB <= 160 * 1024, "fits the LDS of one CU");
 
 extern __shared__ __attribute__((aligned(16))) char pair_smem[];
 
-// 256-byte rows: 16-byte chunk c of row r sits at chunk c ^ f(r), f a
-// bijection of r mod 16.  A 16-lane read of one chunk over 16 consecutive rows
-// hits 16 distinct chunks; a transposing read covers rows {r..r+3, r+8..r+11}
-// (r % 16 in {0, 4}) x one aligned chunk pair, and f >> 1 is distinct over
-// those eight rows, so the pairs land on distinct 32-byte slots.  The LDS
-// serves 256 bytes per cycle to 8- and 16-byte accesses (measured on gfx950).
-__device__ __forceinline__ int fsw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 256-byte rows: 16-byte chunk c of row r sits at chunk c ^ f(r), f a linear
+// bijection of r mod 16 (over GF(2)).  B and x are read two ways: by rows (a
+// 16-byte read of one chunk over 16 consecutive rows) and transposed (rows
+// {r..r+3, r+8..r+11}, r % 16 in {0, 4}, x one aligned chunk pair).  For the
+// transposed reads f >> 1 must be distinct over those eight rows, so that the
+// pairs land on distinct 32-byte slots; which f also keeps the row reads free
+// of bank conflicts was measured on gfx950 (the 16-byte rule is not the plain
+// "distinct 16-byte slots per 16 lanes"): this one, bits
+//   f0 = r0^r2, f1 = r0^r2^r3, f2 = r1, f3 = r2^r3.
+__device__ __forceinline__ int fsw(int r) {
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  return (r0 ^ r2) | ((r0 ^ r2 ^ r3) << 1) | (r1 << 2) | ((r2 ^ r3) << 3);
+}
 __device__ __forceinline__ int tile_off(int r, int c) { return r * kRowB + ((c ^ fsw(r)) << 4); }
-// C is only read by rows, for which the plain row XOR (chunk c of row r at
-// c ^ (r % 16)) is conflict-free on this LDS for both 16-byte reads (one
-// chunk over 16 rows) and pairs of 8-byte reads (measured; f above is not, for
-// 16-byte reads).
+// C is only read by rows: the plain row XOR (chunk c of row r at c ^ (r % 16))
+// is conflict-free for them (measured).
 __device__ __forceinline__ int c_off(int r, int c) { return r * kRowB + ((c ^ (r & 15)) << 4); }
 // M rows are 128 bytes (64 s): chunk c of row t sits at c ^ ((t >> 1) & 7).
 __device__ __forceinline__ int m_off(int t, int c) { return t * 128 + ((c ^ ((t >> 1) & 7)) << 4); }
 
 template <typename T> __device__ __forceinline__ T ld_lds(int off) {
   return *(const __attribute__((address_space(3))) T *)((const lds_char *)pair_smem + off);
-}
-// a read the compiler may not fuse with its neighbours (it would pair reads a
-// multiple of 512 bytes apart into one instruction whose accesses conflict)
-template <typename T> __device__ __forceinline__ T ld_lds_v(int off) {
-  return *(const volatile __attribute__((address_space(3))) T *)((const lds_char *)pair_smem + off);
 }
 template <typename T> __device__ __forceinline__ void st_lds(int off, T v) {
   *(__attribute__((address_space(3))) T *)((lds_char *)pair_smem + off) = v;
@@ -161,16 +160,34 @@ __device__ __forceinline__ int block_end(const ScanArgs &a, const ScanMeta &m, i
   return t1;
 }
 
+// G4's A operand for K = n in [32j, 32j + 32) from the state tiles 2j and
+// 2j+1 (lane group g holds n = 32j + 4g .. +3 and 32j + 16 + 4g .. +3): two
+// row swaps (upper half with lower half, then odd rows with even rows) give
+// lane group g n = 32j + 8g .. +7 in order, the K layout of a 16-byte read
+// of C.
+__device__ __forceinline__ bf16x8_t state_operand(f32x4_t lo_tile, f32x4_t hi_tile) {
+  const u32x2_t a = pk4(lo_tile), b = pk4(hi_tile);
+  u32x4_t o;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const auto s32 = __builtin_amdgcn_permlane32_swap(a[e], b[e], false, false);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+    o[e] = s16[0];      // n = 32j + 8g + 2e .. +1
+    o[2 + e] = s16[1];  // n = 32j + 8g + 4 + 2e .. +1
+  }
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
 // Everything a wave carries from block to block.
 struct Wave {
   // identity
   int lane, li, g, w, q, ps;
   // per-lane LDS byte offsets, fixed for the whole kernel (a buffer, a tile
   // row or a K step adds a constant)
-  int o_c[8];    // C rows (G4, G1): [k][n = 32k + 16 piece + 4g .. +3]
-  int o_b1[8];   // B rows (G1): the same n
+  int o_c[4];    // C rows (G4, G1): n = 32k + 8g .. +7
+  int o_b1[4];   // B rows (G1): the same n
   int o_x[2];    // x, transposing, rows +0 / +4
-  int o_bt[16];  // B^T, transposing: [n tile][rows +0 / +4]
+  int bt_base[2], bt_xor[2];  // B^T, transposing, rows +0 / +4: n tile i at base + (32 i ^ xor)
   int o_m[2];    // M rows for G2, per K step
   int sums;      // this wave's running-sum area
   // staging: per-lane source offsets of full blocks (row 8w + 4u + g)
@@ -179,6 +196,7 @@ struct Wave {
   f32x4_t h[8];  // h^T[n = 16i + 4g + r][p = 16 ps + li]
   f32x4_t y[4];  // y^T[p = 16 ps + 4g + r][t = 16 tt + li]
   bool have_h;
+  float lam;     // exp(cs_end) of the current block, own head
   bool stores4;  // exactly four global stores followed the last input loads
 };
 
@@ -224,8 +242,10 @@ __device__ __forceinline__ Loads prepare_loads(const ScanArgs &a, const Wave &W,
   L.lds = (uint32_t)(uintptr_t)(lds_char *)pair_smem + buf * kTileB + 8 * W.w * kRowB;
   return L;
 }
-// part 0: C and dt; part 1: B; part 2: x
+// part 0: dt (wave 0, first: six copies follow it) and C; part 1: B; part 2: x
 __device__ __forceinline__ void issue_part(const Loads &L, const Wave &W, int part, int buf) {
+  if (part == 0 && W.w == 0)
+    dma4(L.dtb, L.vdt, (uint32_t)(uintptr_t)(lds_char *)pair_smem + kOffDt + buf * Q * 4);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const uint32_t dst = L.lds + 4 * u * kRowB;
@@ -233,8 +253,6 @@ __device__ __forceinline__ void issue_part(const Loads &L, const Wave &W, int pa
     if (part == 1) dma16(L.bb, L.vb[u], kOffB + dst);
     if (part == 2) dma16(L.xb, L.vx[u], kOffX + dst);
   }
-  if (part == 0 && W.w == 0)
-    dma4(L.dtb, L.vdt, (uint32_t)(uintptr_t)(lds_char *)pair_smem + kOffDt + buf * Q * 4);
 }
 
 // Makes the register value available at this point (the compiler waits for
@@ -242,6 +260,90 @@ __device__ __forceinline__ void issue_part(const Loads &L, const Wave &W, int pa
 // of a phase are issued together, ahead of the work that hides their latency.
 template <typename T> __device__ __forceinline__ void pin(T &v) {
   asm volatile("" : "+v"(v)::"memory");
+}
+
+// Keeps the compiler from moving memory operations across this point (it
+// fixes the order in which reads are issued).
+__device__ __forceinline__ void fence() { asm volatile("" ::: "memory"); }
+
+// One 16 x 16 tile of C.B^T (s tile a, t tile b) and the running sums its mask
+// needs, read ahead of its products.
+struct Tile {
+  int a, b;
+  bf16x8_t ga[4], gb[4];
+  float cst[2];
+  f32x4_t cp[2];
+};
+__device__ __forceinline__ Tile tile_load(const Wave &W, int id, int bbuf, int cbuf) {
+  Tile t;
+  t.a = id < 4 ? id : id < 7 ? id - 4 : id == 7 ? 0 : id == 8 ? 1 : 0;
+  t.b = id < 4 ? id : id < 7 ? id - 3 : id == 7 ? 2 : 3;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t.ga[k] = ld_lds<bf16x8_t>(bbuf + t.a * 16 * kRowB + W.o_b1[k]);
+    t.gb[k] = ld_lds<bf16x8_t>(cbuf + t.b * 16 * kRowB + W.o_c[k]);
+  }
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    t.cst[hq] = ld_lds<float>(W.sums + hq * 256 + 4 * (16 * t.b + W.li));
+    t.cp[hq] = ld_lds<f32x4_t>(W.sums + (2 + hq) * 256 + 4 * (16 * t.a + 4 * W.g));
+  }
+  return t;
+}
+// M_q[t][s] = C_t.B_s exp2(cs_t - cs_s) dt_s for both heads, D on the diagonal
+__device__ __forceinline__ void tile_mask(const Wave &W, const Seg &S, Tile &t) {
+  const int li = W.li, g = W.g;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    pin(t.ga[k]);
+    pin(t.gb[k]);
+  }
+  f32x4_t cb = zero4();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cb = mfma(t.ga[k], t.gb[k], cb);
+  // cb[r] = C_t.B_s with t = 16 b + li, s = 16 a + 4 g + r
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    f32x4_t mv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mv[r] = cb[r] * __builtin_amdgcn_exp2f(t.cst[hq] - t.cp[hq][r]);
+    if (t.a == t.b) {
+      // above the diagonal the exponent may overflow: selected away; the skip
+      // term D x[t] rides on the diagonal
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 4 * g + r;
+        mv[r] = s < li ? mv[r] : (s == li ? mv[r] + S.Dq[hq] : 0.f);
+      }
+    }
+    st_lds<u32x2_t>(kOffM + hq * kMHeadB + (16 * t.b + li) * 128 +
+                        (((2 * t.a + (g >> 1)) ^ ((li >> 1) & 7)) << 4) + 8 * (g & 1),
+                    pk4(mv));
+  }
+}
+
+// Running sums of dt*A (log2 units) of a block, one token per lane, both heads,
+// into this wave's area: cs of both heads, cs - log2(dt) of both (the mask's
+// exp2(cs_t - this) carries the dt_s factor; dt = 0, past the block end, gives
+// +inf and a zero weight), exp(cs) and the G3 weights of its own head.
+// Returns exp(cs_end) of its own head.
+__device__ __forceinline__ float block_sums(const Wave &W, const Seg &S, int buf, int len) {
+  const int lane = W.lane;
+  const uint32_t dtw = ld_lds<uint32_t>(kOffDt + buf * Q * 4 + 4 * lane);
+  const float dq0 = lane < len ? __uint_as_float(dtw << 16) : 0.f;
+  const float dq1 = lane < len ? __uint_as_float(dtw & 0xffff0000u) : 0.f;
+  const float c0 = scan64(dq0 * S.al2[0]);
+  const float c1 = scan64(dq1 * S.al2[1]);
+  const float cq = W.q ? c1 : c0, dqq = W.q ? dq1 : dq0;
+  const float endq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cq), 63));
+  const int s = W.sums + 4 * lane;
+  st_lds<float>(s + 0 * 256, c0);
+  st_lds<float>(s + 1 * 256, c1);
+  st_lds<float>(s + 2 * 256, c0 - __builtin_amdgcn_logf(dq0));
+  st_lds<float>(s + 3 * 256, c1 - __builtin_amdgcn_logf(dq1));
+  st_lds<float>(s + 4 * 256, __builtin_amdgcn_exp2f(cq));
+  st_lds<float>(s + 5 * 256, __builtin_amdgcn_exp2f(endq - cq) * dqq);
+  return __builtin_amdgcn_exp2f(endq);
 }
 
 template <int BUF>
@@ -262,58 +364,44 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
   else
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();  // [A] inputs of this block visible; the other buffer is free
-  uint32_t dtw = ld_lds<uint32_t>(kOffDt + BUF * Q * 4 + 4 * W.lane);
-  pin(dtw);
+  const float lam = W.lam;  // this block's sums were written during the previous one
   const Loads nl = prepare_loads(a, W, S, BUF ^ 1, S.n0, S.n1 - S.n0);
 
-  const int lane = W.lane, li = W.li, g = W.g, q = W.q;
+  const int li = W.li, g = W.g, q = W.q;
   const int cbuf = kOffC + BUF * kTileB, bbuf = kOffB + BUF * kTileB, xbuf = kOffX + BUF * kTileB;
 
-  // ---- reads of G4's C operands and of x, in flight during the sums
+  // ---- reads, in the order they are needed: G4's C operands; x, the G3
+  // weights and exp(cs_t); the operands of this wave's first C.B tile
   bf16x8_t op[16];
   if (W.have_h) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        op[4 * tt + j] = cat8(ld_lds_v<u32x2_t>(cbuf + W.o_c[2 * j] + tt * 16 * kRowB),
-                              ld_lds_v<u32x2_t>(cbuf + W.o_c[2 * j + 1] + tt * 16 * kRowB));
+        op[4 * tt + j] = ld_lds<bf16x8_t>(cbuf + W.o_c[j] + tt * 16 * kRowB);
   }
+  fence();
   s16x4_t xr[4];  // x[s = 32k + 8g + 4r + ..][p = 16 ps + li]: [k][r]
 #pragma unroll
   for (int k = 0; k < 2; ++k)
 #pragma unroll
     for (int r = 0; r < 2; ++r) xr[2 * k + r] = ld_tr(xbuf + W.o_x[r] + k * 32 * kRowB);
-
-  // ---- running sums of dt*A (log2 units), one token per lane, both heads
-  const float dq0 = lane < len ? __uint_as_float(dtw << 16) : 0.f;
-  const float dq1 = lane < len ? __uint_as_float(dtw & 0xffff0000u) : 0.f;
-  const float c0 = scan64(dq0 * S.al2[0]);
-  const float c1 = scan64(dq1 * S.al2[1]);
-  const float cq = q ? c1 : c0, dqq = q ? dq1 : dq0;
-  const float endq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cq), 63));
-  const float lam = __builtin_amdgcn_exp2f(endq);
-  {
-    const int s = W.sums + 4 * lane;
-    st_lds<float>(s + 0 * 256, c0);
-    st_lds<float>(s + 1 * 256, c1);
-    // cs_s - log2(dt_s): the mask's exp2(cs_t - this) carries the dt_s
-    // factor; dt = 0 (past the block end) gives +inf and a zero weight
-    st_lds<float>(s + 2 * 256, c0 - __builtin_amdgcn_logf(dq0));
-    st_lds<float>(s + 3 * 256, c1 - __builtin_amdgcn_logf(dq1));
-    st_lds<float>(s + 4 * 256, __builtin_amdgcn_exp2f(cq));
-    st_lds<float>(s + 5 * 256, __builtin_amdgcn_exp2f(endq - cq) * dqq);
-  }
-
-  if (more) issue_part(nl, W, 0, BUF ^ 1);
-  // ---- G4: y^T[p,t] = exp(cs_t) sum_n h_prev[p,n] C[t,n]
+  f32x4_t wv[4];  // w_s, s = 32k + 8g + 4e .. +3: [k][e]
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      wv[2 * k + e] = ld_lds<f32x4_t>(W.sums + 5 * 256 + 4 * (32 * k + 8 * g + 4 * e));
   float ev[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) ev[tt] = ld_lds<float>(W.sums + 4 * 256 + 4 * (16 * tt + li));
+  if (more) issue_part(nl, W, 0, BUF ^ 1);
+
+  // ---- G4: y^T[p,t] = exp(cs_t) sum_n h_prev[p,n] C[t,n]
   if (W.have_h) {
     bf16x8_t ha[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ha[j] = cat8(pk4(W.h[2 * j]), pk4(W.h[2 * j + 1]));
+    for (int j = 0; j < 4; ++j) ha[j] = state_operand(W.h[2 * j], W.h[2 * j + 1]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) pin(op[i]);
 #pragma unroll
@@ -324,75 +412,10 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
       W.y[tt] = acc;
     }
   }
-
-  if (more) issue_part(nl, W, 1, BUF ^ 1);
-  // ---- G1: this wave's tiles of C.B^T (s tile a, t tile b), masked per head
-  // tiles: waves 0..7 take (0,0) (1,1) (2,2) (3,3) (0,1) (1,2) (2,3) (0,2);
-  // waves 0 and 1 also take (1,3) and (0,3)
-  const int ntile = W.w < 2 ? 2 : 1;
-  for (int it = 0; it < ntile; ++it) {
-    const int id = it == 0 ? W.w : 8 + W.w;
-    const int a_t = id < 4 ? id : id < 7 ? id - 4 : id == 7 ? 0 : id == 8 ? 1 : 0;
-    const int b_t = id < 4 ? id : id < 7 ? id - 3 : id == 7 ? 2 : 3;
-    bf16x8_t ga[4], gb[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ga[k] = cat8(ld_lds<u32x2_t>(bbuf + a_t * 16 * kRowB + W.o_b1[2 * k]),
-                   ld_lds<u32x2_t>(bbuf + a_t * 16 * kRowB + W.o_b1[2 * k + 1]));
-      gb[k] = cat8(ld_lds<u32x2_t>(cbuf + b_t * 16 * kRowB + W.o_c[2 * k]),
-                   ld_lds<u32x2_t>(cbuf + b_t * 16 * kRowB + W.o_c[2 * k + 1]));
-    }
-    float cst[2];
-    f32x4_t cp[2];
-#pragma unroll
-    for (int hq = 0; hq < 2; ++hq) {
-      cst[hq] = ld_lds<float>(W.sums + hq * 256 + 4 * (16 * b_t + li));
-      cp[hq] = ld_lds<f32x4_t>(W.sums + (2 + hq) * 256 + 4 * (16 * a_t + 4 * g));
-    }
-    f32x4_t cb = zero4();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) cb = mfma(ga[k], gb[k], cb);
-    // cb[r] = C_t.B_s with t = 16 b + li, s = 16 a + 4 g + r
-#pragma unroll
-    for (int hq = 0; hq < 2; ++hq) {
-      f32x4_t mv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mv[r] = cb[r] * __builtin_amdgcn_exp2f(cst[hq] - cp[hq][r]);
-      if (a_t == b_t) {
-        // above the diagonal the exponent may overflow: selected away; the
-        // skip term D x[t] rides on the diagonal
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = 4 * g + r;
-          mv[r] = s < li ? mv[r] : (s == li ? mv[r] + S.Dq[hq] : 0.f);
-        }
-      }
-      st_lds<u32x2_t>(kOffM + hq * kMHeadB + (16 * b_t + li) * 128 +
-                          (((2 * a_t + (g >> 1)) ^ ((li >> 1) & 7)) << 4) + 8 * (g & 1),
-                      pk4(mv));
-    }
-  }
-  if (W.have_h) {
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) W.y[tt] *= ev[tt];
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) W.y[tt] = zero4();
-  }
-
-  if (more) issue_part(nl, W, 2, BUF ^ 1);
-  // ---- G3: h^T <- lam h^T + B^T (w x); B^T operands in two halves of n
-  f32x4_t wv[4];
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) wv[2 * k + e] = ld_lds<f32x4_t>(W.sums + 5 * 256 + 4 * (32 * k + 8 * g + 4 * e));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      op[2 * i + k] = cat8(ld_tr(bbuf + W.o_bt[2 * i] + k * 32 * kRowB),
-                           ld_tr(bbuf + W.o_bt[2 * i + 1] + k * 32 * kRowB));
+  // G1 tiles: waves 0..7 take (s tile a, t tile b) = (0,0) (1,1) (2,2) (3,3)
+  // (0,1) (1,2) (2,3) (0,2); waves 0 and 1 also take (1,3) and (0,3)
+  Tile t0 = tile_load(W, W.w, bbuf, cbuf);
+  // ---- x and w x (G3's B operand), beside G4's products
   bf16x8_t xk[2], xt[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -411,26 +434,39 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
                         __uint_as_float(xv[e] & 0xffff0000u) * w8[2 * e + 1]);
     xt[k] = __builtin_bit_cast(bf16x8_t, o);
   }
+
+  // ---- G1: C.B^T tiles masked per head into M
+  tile_mask(W, S, t0);
+  if (more) issue_part(nl, W, 1, BUF ^ 1);
+  if (W.w < 2) {
+    Tile t1 = tile_load(W, 8 + W.w, bbuf, cbuf);
+    tile_mask(W, S, t1);
+  }
+  if (W.have_h) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) W.y[tt] *= ev[tt];
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) W.y[tt] = zero4();
+  }
+
+  // ---- G3: h^T <- lam h^T + B^T (w x)
+  if (more) issue_part(nl, W, 2, BUF ^ 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      op[2 * i + k] = cat8(ld_tr(bbuf + W.bt_base[0] + ((32 * i) ^ W.bt_xor[0]) + k * 32 * kRowB),
+                           ld_tr(bbuf + W.bt_base[1] + ((32 * i) ^ W.bt_xor[1]) + k * 32 * kRowB));
 #pragma unroll
   for (int i = 0; i < 8; ++i) W.h[i] *= lam;
 #pragma unroll
-  for (int i = 4; i < 8; ++i)
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      op[2 * i + k] = cat8(ld_tr(bbuf + W.o_bt[2 * i] + k * 32 * kRowB),
-                           ld_tr(bbuf + W.o_bt[2 * i + 1] + k * 32 * kRowB));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) pin(op[i]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i) {
+    pin(op[2 * i]);
+    pin(op[2 * i + 1]);
 #pragma unroll
     for (int k = 0; k < 2; ++k) W.h[i] = mfma(op[2 * i + k], xt[k], W.h[i]);
-#pragma unroll
-  for (int i = 8; i < 16; ++i) pin(op[i]);
-#pragma unroll
-  for (int i = 4; i < 8; ++i)
-#pragma unroll
-    for (int k = 0; k < 2; ++k) W.h[i] = mfma(op[2 * i + k], xt[k], W.h[i]);
+  }
 
   // checkpoints: the post-token state of t1 - 1
   const int hh = S.h0 + q;
@@ -444,7 +480,9 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
   }
   W.have_h = true;
   S.ck = ck_next;
-  lds_barrier();  // [B] M is written
+  // the next block's dt has landed (wave 0 issued it before six more copies)
+  if (more && W.w == 0) __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  lds_barrier();  // [B] M is written; the next block's dt is visible
 
   // ---- G2: y^T[p,t] += sum_s x^T[p,s] M^T[s,t], s <= t
   const int mb = kOffM + q * kMHeadB;
@@ -453,6 +491,8 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
   for (int tt = 0; tt < 4; ++tt) mo[tt] = ld_lds<bf16x8_t>(mb + tt * 16 * 128 + W.o_m[0]);
 #pragma unroll
   for (int tt = 2; tt < 4; ++tt) mo[2 + tt] = ld_lds<bf16x8_t>(mb + tt * 16 * 128 + W.o_m[1]);
+  // the next block's sums, while M is read (this block's were last read by G3)
+  if (more) W.lam = block_sums(W, S, BUF ^ 1, S.n1 - S.n0);
 #pragma unroll
   for (int i = 0; i < 6; ++i) pin(mo[i]);
 #pragma unroll
@@ -500,19 +540,18 @@ __global__ __launch_bounds__(kPairThreads, 1) void scan_ssd_pair_kernel(ScanArgs
 
   // ---- per-lane LDS offsets
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int piece = 0; piece < 2; ++piece) {  // n = 32k + 16 piece + 4g .. +3 of row li
-      W.o_c[2 * k + piece] = c_off(li, 4 * k + 2 * piece + (g >> 1)) + 8 * (g & 1);
-      W.o_b1[2 * k + piece] = tile_off(li, 4 * k + 2 * piece + (g >> 1)) + 8 * (g & 1);
-    }
+  for (int k = 0; k < 4; ++k) {  // n = 32k + 8g .. +7 of row li
+    W.o_c[k] = c_off(li, 4 * k + g);
+    W.o_b1[k] = tile_off(li, 4 * k + g);
+  }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int row = 8 * g + 4 * r + (li >> 2);
     W.o_x[r] = tile_off(row, 8 * W.q + 2 * W.ps + ((li >> 1) & 1)) + 8 * (li & 1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      W.o_bt[2 * i + r] = tile_off(row, 2 * i + ((li >> 1) & 1)) + 8 * (li & 1);
+    // chunk 2i + b of the row sits at (2i + b) ^ f = 2 (i ^ (f >> 1)) + (b ^ (f & 1))
+    const int f = fsw(row), b = (li >> 1) & 1;
+    W.bt_base[r] = row * kRowB + 16 * (b ^ (f & 1)) + 8 * (li & 1);
+    W.bt_xor[r] = 32 * (f >> 1);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) W.o_m[k] = m_off(li, 4 * k + g);
@@ -562,6 +601,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void scan_ssd_pair_kernel(ScanArgs
     issue_part(l0, W, 1, 0);
     issue_part(l0, W, 2, 0);
   }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  W.lam = block_sums(W, S, 0, S.t1 - S.t0);
   W.stores4 = false;
 
   while (pair_block<0>(a, m, W, S) && pair_block<1>(a, m, W, S)) {
