@@ -41,23 +41,23 @@ MIB = 1 << 20
 # figure into null until the counters are taken again.
 DECODE_COUNTERS = {
     "sources": ["ssm_decode.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "74e9a1112cb7647d4691763fb9f0d14506481a6b4fdd70c307ffc2f72672107e",
-    "fetch_kib": 519888.69, "write_kib": 1056770.73,
+    "sha256": "ba4a931c0511166a8a83db12b93a7ab301b4be4390f48245464bb7ac97bac047",
+    "fetch_kib": 519889.04, "write_kib": 1056770.55,
     "calib_fetch_kib": 2059.01, "calib_write_kib": 4096.0, "calib_true_kib": 4096.0,
     "algorithmic_kib": 1035989.33 + 1056768.0,
 }
 
 
 # The same for scan_ssd_pair_kernel on the 65,536-token prefill (mean per dispatch
-# over 4 dispatches): MFMA busy cycles summed over all SIMDs, GPU-active
+# over 6 dispatches): MFMA busy cycles summed over all SIMDs, GPU-active
 # cycles summed over the 8 XCDs, bf16 MFMA operations (x512 = flops), and the
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
     "sources": ["ssm_ssd_pair.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "dcb2361100bbed7cff246ff0d9b143e50bbf9312b6497ab9d9f7bb99f4601550",
-    "mfma_busy_cycles": 420020224.0, "gui_active_cycles": 19655994.67, "xcds": 8, "simds": 1024,
-    "mfma_mops_bf16": 840040448.0,
-    "fetch_kib": 740561.95, "write_kib": 1085440.93,
+    "sha256": "754b73d0c5ea488938dea67451e9a76e880a5781a2962ae4fd1c94a3c6200980",
+    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14376120.83, "xcds": 8, "simds": 1024,
+    "mfma_mops_bf16": 722141184.0,
+    "fetch_kib": 721040.01, "write_kib": 1085440.17,
     "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2**25 + 2 * 2**22,
 }
 
@@ -66,8 +66,8 @@ PREFILL_COUNTERS = {
 # steps, from the log lengths, averaged).
 REPLAY_COUNTERS = {
     "sources": ["ssm_kernels.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "d3f5df0d206cce720595115d8689ea3c5ccdc2a312157a5b3d26342a1fcf0f88",
-    "fetch_kib": 577234.83, "write_kib": 208579.74,
+    "sha256": "1bb3c309cd0f6dfc648d54aa21b5f19a80d9b8a44876a16b4610a53020be2b32",
+    "fetch_kib": 577233.12, "write_kib": 208581.34,
     "algorithmic_bytes": 1375888554.67,
 }
 
