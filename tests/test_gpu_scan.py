@@ -137,6 +137,41 @@ def test_ragged_resets_checkpoints(ssm, H, P, N, G, io, L):
     assert h.position(1) == (ref["pos"], 1) and ref["pos"] == L - (2 * L) // 3
 
 
+def test_mfma_form_dt_not_word_aligned(ssm):
+    """The head-pair MFMA kernel reads dt of a head pair as one 32-bit word;
+    a dt buffer that starts on an odd bf16 element takes the one-head kernel.
+    Both forms must give the oracle's results (here with a reset and
+    checkpoints), and the outputs of the two must agree closely."""
+    H, P, N, G, L = 4, 64, 128, 1, 150
+    say("scan dt offset by one element", H, L)
+    x, dt, B, C = inputs.tokens(32, L, H, P, N, G)
+    A, D = inputs.params(32, H)
+    bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
+    x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
+    dx, ddt, dB, dC = [bf16_dev(a) for a in bits]
+    # the same dt values behind a one-element offset: 2-byte but not 4-byte aligned
+    padded = torch.zeros(L * H + 1, dtype=torch.bfloat16, device="cuda")
+    padded[1:] = ddt.reshape(-1)
+    ddt_odd = padded[1:].view(L, H)
+    assert ddt_odd.data_ptr() % 4 == 2 and ddt.data_ptr() % 4 == 0
+    reset = np.zeros(L, np.uint8)
+    reset[70] = 1
+    ck = [10, 69, 149]
+    ref = oracle.scan(x, dt, B, C, A, D, reset=reset, ckpt_at=ck)
+    outs = []
+    for d_ in (ddt, ddt_odd):
+        h = ssm.StreamState(H, P, N, 1, to_dev(A), to_dev(D), G=G, io_dtype="bf16")
+        h.reset([0])
+        y, cko = h.scan_chunk(0, 0, dx, d_, dB, dC, reset=reset, ckpt_at=ck)
+        torch.cuda.synchronize()
+        assert_close(host(y), ref["y"], what="y", **bf16_tol(ref["y"]))
+        assert_close(host(cko), ref["ckpt"], what="checkpoints", **bf16_tol(ref["ckpt"]))
+        outs.append((host(y), host(h.state[0])))
+        h.destroy()
+    assert_close(outs[0][0], outs[1][0], what="pair vs one-head y", **bf16_tol(outs[1][0]))
+    assert_close(outs[0][1], outs[1][1], what="pair vs one-head state", **bf16_tol(outs[1][1]))
+
+
 @pytest.mark.parametrize("H,P,N,G,io,L,resets,ck", [
     # resets inside tiles (one doubled, one on a checkpoint token), checkpoints
     # on tile edges and on the last token
