@@ -54,7 +54,7 @@ DECODE_COUNTERS = {
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
     "sources": ["ssm_ssd_pair.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "754b73d0c5ea488938dea67451e9a76e880a5781a2962ae4fd1c94a3c6200980",
+    "sha256": "0baeddb25f3b5f9f3f637c15d0f0e092e9bb180ccd620710977c18889dc8843a",
     "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14376120.83, "xcds": 8, "simds": 1024,
     "mfma_mops_bf16": 722141184.0,
     "fetch_kib": 721040.01, "write_kib": 1085440.17,

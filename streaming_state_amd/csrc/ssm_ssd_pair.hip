@@ -24,11 +24,15 @@
 //
 // Inputs reach LDS by direct global->LDS loads (no registers on the way),
 // double buffered: the next block's loads are in flight while this block
-// computes.  They are issued from inline assembly, so the compiler, which
-// cannot tell which LDS bytes such a load writes, does not make every LDS read
-// of the current block wait for them; the kernel waits for them itself (an
-// explicit vmcnt before the first barrier of the next block).  Two barriers
-// per block: inputs landed; M written.  ~124 KiB of LDS, one workgroup per CU.
+// computes, issued in three parts spread over its phases.  They are issued
+// from inline assembly, so the compiler, which cannot tell which LDS bytes
+// such a load writes, does not make every LDS read of the current block wait
+// for them; the kernel waits for them itself (an explicit vmcnt before the
+// first barrier of the next block).  Two barriers per block: inputs landed; M
+// written.  The next block's running sums are computed after the second, while
+// M is read.  Each phase issues its reads together, ahead of the work that
+// hides their latency.  ~124 KiB of LDS, one workgroup per CU, two waves per
+// SIMD.
 //
 // MFMA 16x16x32 operand layout: lane l supplies row (A) or column (B) l%16 and
 // eight K values; which K a register slot carries is the same for A and B,
