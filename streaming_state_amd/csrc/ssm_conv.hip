@@ -42,33 +42,6 @@ template <typename T> struct Vec<T, 4> {
   }
 };
 
-template <> struct Vec<bf16_t, 8> {
-  static __device__ __forceinline__ void ld(const bf16_t *p, float *v) {
-    const uint4 r = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  static __device__ __forceinline__ void st(bf16_t *p, const float *v) {
-    uint4 r;
-    r.x = pack2_bf16(v[0], v[1]);
-    r.y = pack2_bf16(v[2], v[3]);
-    r.z = pack2_bf16(v[4], v[5]);
-    r.w = pack2_bf16(v[6], v[7]);
-#if SSM_CONV_NT
-    __builtin_nontemporal_store(r.x, reinterpret_cast<uint32_t *>(p));
-    __builtin_nontemporal_store(r.y, reinterpret_cast<uint32_t *>(p) + 1);
-    __builtin_nontemporal_store(r.z, reinterpret_cast<uint32_t *>(p) + 2);
-    __builtin_nontemporal_store(r.w, reinterpret_cast<uint32_t *>(p) + 3);
-#else
-    *reinterpret_cast<uint4 *>(p) = r;
-#endif
-  }
-};
-
 // Raw V-element vectors (bf16 stays packed in registers until used).
 template <typename T, int V> struct Raw;
 template <> struct Raw<float, 4> {
@@ -88,15 +61,6 @@ template <> struct Raw<bf16_t, 4> {
   }
   static __device__ __forceinline__ type zero() { return make_uint2(0u, 0u); }
 };
-template <> struct Raw<bf16_t, 8> {
-  typedef uint4 type;
-  static __device__ __forceinline__ type ld(const bf16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-  static __device__ __forceinline__ float get(const type &r, int v) {
-    const uint32_t w = v < 2 ? r.x : v < 4 ? r.y : v < 6 ? r.z : r.w;
-    return __uint_as_float((v & 1) ? (w & 0xffff0000u) : (w << 16));
-  }
-  static __device__ __forceinline__ type zero() { return make_uint4(0u, 0u, 0u, 0u); }
-};
 template <typename T> struct Raw<T, 1> {
   typedef T type;
   static __device__ __forceinline__ type ld(const T *p) { return *p; }
@@ -105,16 +69,7 @@ template <typename T> struct Raw<T, 1> {
 };
 // Tokens per thread in the chunk kernel: all of a thread's inputs (its tokens
 // and the K-1 before them) are loaded before any output is stored.
-#ifndef SSM_CONV_RUN
-#define SSM_CONV_RUN 16
-#endif
-#ifndef SSM_CONV_NT
-#define SSM_CONV_NT 0
-#endif
-#ifndef SSM_CONV_V8
-#define SSM_CONV_V8 0
-#endif
-constexpr int kConvRun = SSM_CONV_RUN;
+constexpr int kConvRun = 16;
 
 // Grid (channel groups of blockDim.x * V, token runs of kConvRun).  The K-1
 // window entries before the run are held as fp32 (they may come from the
@@ -276,10 +231,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(const T *y, const T *z, 
 // computed once and kept in registers (kGateRegs vectors per thread) while
 // the group's sum of squares is reduced; groups larger than that take two
 // passes, recomputing g from y and z (still in L2) in the second.
-#ifndef SSM_GATE_REGS
-#define SSM_GATE_REGS 8
-#endif
-constexpr int kGateRegs = SSM_GATE_REGS;
+constexpr int kGateRegs = 8;
 
 __device__ __forceinline__ float block_sum(float v, float *part) {
 #pragma unroll
@@ -403,12 +355,7 @@ template <typename T, int K>
 hipError_t conv_chunk_k(const ConvArgs &a, const ConvChunkMeta &m, hipStream_t s) {
   const int runs = (a.t_end - a.t_begin + kConvRun - 1) / kConvRun;
   const bool v4 = a.C % 4 == 0 && ((((uintptr_t)a.x | (uintptr_t)a.y) & (4 * sizeof(T) - 1)) == 0);
-  const bool v8 = sizeof(T) == 2 && a.C % 8 == 0 && ((((uintptr_t)a.x | (uintptr_t)a.y) & 15) == 0);
-  if (SSM_CONV_V8 && v8) {
-    const int b = fit_block(a.C / 8);
-    dim3 grid((a.C / 8 + b - 1) / b, runs);
-    hipLaunchKernelGGL((conv_chunk_kernel<bf16_t, K, 8>), grid, dim3(b), 0, s, a, m);
-  } else if (v4) {
+  if (v4) {
     const int b = fit_block(a.C / 4);
     dim3 grid((a.C / 4 + b - 1) / b, runs);
     hipLaunchKernelGGL((conv_chunk_kernel<T, K, 4>), grid, dim3(b), 0, s, a, m);
