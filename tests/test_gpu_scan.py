@@ -172,6 +172,41 @@ def test_mfma_form_dt_not_word_aligned(ssm):
     assert_close(outs[0][1], outs[1][1], what="pair vs one-head state", **bf16_tol(outs[1][1]))
 
 
+@pytest.mark.parametrize("carry", [True, False])
+def test_mfma_form_many_segments_across_launches(ssm, carry):
+    """The head-pair MFMA kernel over more segments than one launch takes
+    (40 resets: runs of one token, back-to-back resets, a reset on the last
+    token), with checkpoints on both sides of the launch split and just before
+    resets.  With a carried-in state and resets later in the chunk the carry
+    goes through the workspace; without, the chunk opens with a reset."""
+    H, P, N, G, L = 4, 64, 128, 1, 700
+    say("scan many segments", carry)
+    x, dt, B, C = inputs.tokens(33, L, H, P, N, G)
+    A, D = inputs.params(33, H)
+    bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
+    x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
+    dev = [bf16_dev(a) for a in bits]
+    r = np.random.default_rng(33)
+    rs = set(r.choice(np.arange(2, L - 1), 34, replace=False).tolist())
+    rs |= {5, 6, 7, 300, 301, L - 1}
+    if not carry:
+        rs.add(0)
+    reset = np.zeros(L, np.uint8)
+    reset[sorted(rs)] = 1
+    assert int(reset.sum()) >= 40
+    ck = sorted({4, 6, 299, 300, 450, 698, L - 1} | {int(t) for t in r.choice(L, 12, replace=False)})
+    st0 = (r.standard_normal((H, P, N)) * 0.05).astype(np.float32)
+    ref = oracle.scan(x, dt, B, C, A, D, state=st0 if carry else None, reset=reset, ckpt_at=ck)
+    h = ssm.StreamState(H, P, N, 2, to_dev(A), to_dev(D), G=G, io_dtype="bf16")
+    h.init([1], to_dev(st0[None]))
+    y, cko = h.scan_chunk(1, 0, *dev, reset=reset, ckpt_at=ck)
+    torch.cuda.synchronize()
+    assert_close(host(y), ref["y"], what="y", **bf16_tol(ref["y"]))
+    assert_close(host(cko), ref["ckpt"], what="checkpoints", **bf16_tol(ref["ckpt"]))
+    assert_close(host(h.state[1]), ref["state"], what="carry-out", **bf16_tol(ref["state"]))
+    h.destroy()
+
+
 @pytest.mark.parametrize("H,P,N,G,io,L,resets,ck", [
     # resets inside tiles (one doubled, one on a checkpoint token), checkpoints
     # on tile edges and on the last token
