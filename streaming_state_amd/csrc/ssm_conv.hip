@@ -42,6 +42,32 @@ template <typename T> struct Vec<T, 4> {
   }
 };
 
+template <> struct Vec<bf16_t, 8> {
+  static __device__ __forceinline__ void ld(const bf16_t *p, float *v) {
+    const uint4 r = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void st(bf16_t *p, const float *v) {
+    uint4 r;
+    r.x = pack2_bf16(v[0], v[1]);
+    r.y = pack2_bf16(v[2], v[3]);
+    r.z = pack2_bf16(v[4], v[5]);
+    r.w = pack2_bf16(v[6], v[7]);
+    *reinterpret_cast<uint4 *>(p) = r;
+  }
+};
+template <> struct Vec<float, 8> {
+  static __device__ __forceinline__ void ld(const float *p, float *v) {
+    Vec<float, 4>::ld(p, v);
+    Vec<float, 4>::ld(p + 4, v + 4);
+  }
+};
+
 // Raw V-element vectors (bf16 stays packed in registers until used).
 template <typename T, int V> struct Raw;
 template <> struct Raw<float, 4> {
@@ -228,9 +254,10 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(const T *y, const T *z, 
 }
 
 // Gated group RMS norm: one workgroup per (row, group).  g = y * SiLU(z) is
-// computed once and kept in registers (kGateRegs vectors per thread) while
-// the group's sum of squares is reduced; groups larger than that take two
-// passes, recomputing g from y and z (still in L2) in the second.
+// computed once and kept in registers (32 values per thread) while the
+// group's sum of squares is reduced; groups larger than that take two passes,
+// recomputing g from y and z (still in L2) in the second.  bf16 groups of a
+// multiple of 8 use 16-byte vectors.
 constexpr int kGateRegs = 8;
 
 __device__ __forceinline__ float block_sum(float v, float *part) {
@@ -252,11 +279,19 @@ __global__ __launch_bounds__(kThreads) void gate_norm_kernel(const T *y, const T
   const size_t base = (size_t)blockIdx.x * C + (size_t)blockIdx.y * group;
   const float *wg = w + (size_t)blockIdx.y * group;
   const int nv = group / V;  // vectors in the group
-  if (nv <= kThreads * kGateRegs) {
-    float g[kGateRegs][V];
+  constexpr int kRegs = kGateRegs * 4 / V;
+  if (nv <= kThreads * kRegs) {
+    float g[kRegs][V];
     float ss = 0.f;
+    // the weights (shared by every row, so L2 hits) are in flight with y and z
+    float wv[kRegs][V];
 #pragma unroll
-    for (int u = 0; u < kGateRegs; ++u) {
+    for (int u = 0; u < kRegs; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      if (i < nv) Vec<float, V>::ld(wg + (size_t)i * V, wv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRegs; ++u) {
       const int i = threadIdx.x + u * kThreads;
       float yv[V], zv[V];
       if (i < nv) {
@@ -273,15 +308,8 @@ __global__ __launch_bounds__(kThreads) void gate_norm_kernel(const T *y, const T
       }
     }
     const float inv = rsqrtf(block_sum(ss, part) / (float)group + eps);
-    // the weights (shared by every row, so L2 hits) are loaded before any store
-    float wv[kGateRegs][V];
 #pragma unroll
-    for (int u = 0; u < kGateRegs; ++u) {
-      const int i = threadIdx.x + u * kThreads;
-      if (i < nv) Vec<float, V>::ld(wg + (size_t)i * V, wv[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kGateRegs; ++u) {
+    for (int u = 0; u < kRegs; ++u) {
       const int i = threadIdx.x + u * kThreads;
       if (i < nv) {
         float o[V];
@@ -421,7 +449,11 @@ hipError_t gate_t(int64_t rows, int C, int group, const void *y, const void *z, 
     return hipGetLastError();
   }
   const dim3 grid((unsigned)rows, C / group);
-  if (group % 4 == 0 && aligned4 && ((uintptr_t)w & 15) == 0)
+  if (sizeof(T) == 2 && group % 8 == 0 &&
+      ((((uintptr_t)y | (uintptr_t)z | (uintptr_t)out | (uintptr_t)w)) & 15) == 0)
+    hipLaunchKernelGGL((gate_norm_kernel<bf16_t, 8>), grid, dim3(kThreads), 0, s,
+                       (const bf16_t *)y, (const bf16_t *)z, w, C, group, eps, (bf16_t *)out);
+  else if (group % 4 == 0 && aligned4 && ((uintptr_t)w & 15) == 0)
     hipLaunchKernelGGL((gate_norm_kernel<T, 4>), grid, dim3(kThreads), 0, s, yp, zp, w, C, group,
                        eps, op);
   else

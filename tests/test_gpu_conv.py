@@ -127,6 +127,8 @@ def test_conv_decode_vs_oracle(ssm, io):
     (64, 512, 128, "bf16", True),
     (7, 50, 25, "f32", True),     # one element per thread
     (16, 1536, 1536, "f32", True),
+    (5, 24, 8, "bf16", True),        # 16-byte vectors, one per group
+    (4, 16384, 16384, "bf16", True),  # 16-byte vectors, a group past the registers: two passes
 ])
 def test_gate_vs_oracle(ssm, rows, C, group, io, norm):
     say("gate", rows, C, group, io, norm)
