@@ -54,10 +54,10 @@ DECODE_COUNTERS = {
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
     "sources": ["ssm_ssd_pair.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "0baeddb25f3b5f9f3f637c15d0f0e092e9bb180ccd620710977c18889dc8843a",
-    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14376120.83, "xcds": 8, "simds": 1024,
+    "sha256": "56148462b010cb5cf2003408ebbf230eeb08b4b5612289870b8a5d046942fc81",
+    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14312899.17, "xcds": 8, "simds": 1024,
     "mfma_mops_bf16": 722141184.0,
-    "fetch_kib": 721040.01, "write_kib": 1085440.17,
+    "fetch_kib": 721036.72, "write_kib": 1085440.21,
     "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2**25 + 2 * 2**22,
 }
 

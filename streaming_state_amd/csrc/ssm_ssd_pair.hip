@@ -201,6 +201,7 @@ struct Wave {
   f32x4_t y[4];  // y^T[p = 16 ps + 4g + r][t = 16 tt + li]
   bool have_h;
   float lam;     // exp(cs_end) of the current block, own head
+  bool neg;      // some dt of the current block is negative (either head)
   bool stores4;  // exactly four global stores followed the last input loads
 };
 
@@ -294,8 +295,10 @@ __device__ __forceinline__ Tile tile_load(const Wave &W, int id, int bbuf, int c
   }
   return t;
 }
-// M_q[t][s] = C_t.B_s exp2(cs_t - cs_s) dt_s for both heads, D on the diagonal
-__device__ __forceinline__ void tile_mask(const Wave &W, const Seg &S, Tile &t) {
+// M_q[t][s] = C_t.B_s exp2(cs_t - cs_s) dt_s for both heads, D on the diagonal.
+// |dt_s| rides in the exponent; a block with a negative dt takes its sign from
+// the block's dt in LDS (dtbuf).
+__device__ __forceinline__ void tile_mask(const Wave &W, const Seg &S, Tile &t, int dtbuf) {
   const int li = W.li, g = W.g;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -311,6 +314,12 @@ __device__ __forceinline__ void tile_mask(const Wave &W, const Seg &S, Tile &t) 
     f32x4_t mv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) mv[r] = cb[r] * __builtin_amdgcn_exp2f(t.cst[hq] - t.cp[hq][r]);
+    if (W.neg) {  // dt of both heads, tokens s = 16 a + 4 g + r
+      const u32x4_t dw = ld_lds<u32x4_t>(dtbuf + 4 * (16 * t.a + 4 * g));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        mv[r] = __uint_as_float(__float_as_uint(mv[r]) ^ ((hq ? dw[r] : dw[r] << 16) & 0x80000000u));
+    }
     if (t.a == t.b) {
       // above the diagonal the exponent may overflow: selected away; the skip
       // term D x[t] rides on the diagonal
@@ -327,11 +336,12 @@ __device__ __forceinline__ void tile_mask(const Wave &W, const Seg &S, Tile &t) 
 }
 
 // Running sums of dt*A (log2 units) of a block, one token per lane, both heads,
-// into this wave's area: cs of both heads, cs - log2(dt) of both (the mask's
-// exp2(cs_t - this) carries the dt_s factor; dt = 0, past the block end, gives
-// +inf and a zero weight), exp(cs) and the G3 weights of its own head.
-// Returns exp(cs_end) of its own head.
-__device__ __forceinline__ float block_sums(const Wave &W, const Seg &S, int buf, int len) {
+// into this wave's area: cs of both heads, cs - log2|dt| of both (the mask's
+// exp2(cs_t - this) carries the |dt_s| factor; dt = 0, past the block end,
+// gives +inf and a zero weight), exp(cs) and the G3 weights of its own head.
+// Sets W.neg when a dt of the block is negative; returns exp(cs_end) of its
+// own head.
+__device__ __forceinline__ float block_sums(Wave &W, const Seg &S, int buf, int len) {
   const int lane = W.lane;
   const uint32_t dtw = ld_lds<uint32_t>(kOffDt + buf * Q * 4 + 4 * lane);
   const float dq0 = lane < len ? __uint_as_float(dtw << 16) : 0.f;
@@ -343,8 +353,9 @@ __device__ __forceinline__ float block_sums(const Wave &W, const Seg &S, int buf
   const int s = W.sums + 4 * lane;
   st_lds<float>(s + 0 * 256, c0);
   st_lds<float>(s + 1 * 256, c1);
-  st_lds<float>(s + 2 * 256, c0 - __builtin_amdgcn_logf(dq0));
-  st_lds<float>(s + 3 * 256, c1 - __builtin_amdgcn_logf(dq1));
+  st_lds<float>(s + 2 * 256, c0 - __builtin_amdgcn_logf(fabsf(dq0)));
+  st_lds<float>(s + 3 * 256, c1 - __builtin_amdgcn_logf(fabsf(dq1)));
+  W.neg = __builtin_amdgcn_ballot_w64(dq0 < 0.f || dq1 < 0.f) != 0;
   st_lds<float>(s + 4 * 256, __builtin_amdgcn_exp2f(cq));
   st_lds<float>(s + 5 * 256, __builtin_amdgcn_exp2f(endq - cq) * dqq);
   return __builtin_amdgcn_exp2f(endq);
@@ -440,11 +451,11 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
   }
 
   // ---- G1: C.B^T tiles masked per head into M
-  tile_mask(W, S, t0);
+  tile_mask(W, S, t0, kOffDt + BUF * Q * 4);
   if (more) issue_part(nl, W, 1, BUF ^ 1);
   if (W.w < 2) {
     Tile t1 = tile_load(W, 8 + W.w, bbuf, cbuf);
-    tile_mask(W, S, t1);
+    tile_mask(W, S, t1, kOffDt + BUF * Q * 4);
   }
   if (W.have_h) {
 #pragma unroll

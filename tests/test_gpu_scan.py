@@ -172,6 +172,39 @@ def test_mfma_form_dt_not_word_aligned(ssm):
     assert_close(outs[0][1], outs[1][1], what="pair vs one-head state", **bf16_tol(outs[1][1]))
 
 
+def test_mfma_form_negative_dt(ssm):
+    """A finite negative dt is accepted (the pages give no rule against it):
+    the head-pair kernel carries |dt| in the mask's exponent and takes the
+    sign from dt itself.  Negative runs in one head only, in both heads, and
+    across a block boundary, with a reset and checkpoints."""
+    H, P, N, G, L = 4, 64, 128, 1, 300
+    say("scan negative dt", H, L)
+    x, dt, B, C = inputs.tokens(34, L, H, P, N, G)
+    A, D = inputs.params(34, H)
+    dt = dt.copy()
+    dt[10:15, 1] = -0.02          # head 1 of the first pair only
+    dt[60:70, 2:4] = -0.02        # both heads of the second pair, across blocks 0 and 1
+    dt[130, :] = -0.02            # every head, one token
+    dt[200:204, 0] = -0.02        # right after the reset below
+    bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
+    x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
+    assert (dt < 0).sum() == 5 + 20 + 4 + 4
+    dev = [bf16_dev(a) for a in bits]
+    reset = np.zeros(L, np.uint8)
+    reset[200] = 1
+    ck = [14, 69, 130, 199, 203, 299]
+    ref = oracle.scan(x, dt, B, C, A, D, reset=reset, ckpt_at=ck)
+    h = ssm.StreamState(H, P, N, 1, to_dev(A), to_dev(D), G=G, io_dtype="bf16")
+    h.reset([0])
+    y, cko = h.scan_chunk(0, 0, *dev, reset=reset, ckpt_at=ck)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    assert_close(host(y), ref["y"], what="y", **bf16_tol(ref["y"]))
+    assert_close(host(cko), ref["ckpt"], what="checkpoints", **bf16_tol(ref["ckpt"]))
+    assert_close(host(h.state[0]), ref["state"], what="carry-out", **bf16_tol(ref["state"]))
+    h.destroy()
+
+
 @pytest.mark.parametrize("carry", [True, False])
 def test_mfma_form_many_segments_across_launches(ssm, carry):
     """The head-pair MFMA kernel over more segments than one launch takes
