@@ -172,6 +172,38 @@ def test_mfma_form_dt_not_word_aligned(ssm):
     assert_close(outs[0][1], outs[1][1], what="pair vs one-head state", **bf16_tol(outs[1][1]))
 
 
+@pytest.mark.parametrize("ws", [None, "serial"])
+def test_fp32_forms_negative_dt(ssm, ws):
+    """fp32 scan with some negative dt values: the tile-parallel form (ws
+    None) and the recurrent form ("serial") against the oracle, then decode
+    steps with negative dt from the carried state."""
+    H, P, N, G, L = 2, 64, 128, 1, 300
+    say("fp32 negative dt", ws)
+    x, dt, B, C = inputs.tokens(35, L + 4, H, P, N, G)
+    A, D = inputs.params(35, H)
+    dt = dt.copy()
+    dt[20:26, 0] = -0.02
+    dt[100:140, :] = -0.01
+    dt[L + 1:, 1] = -0.02
+    h = ssm.StreamState(H, P, N, 1, to_dev(A), to_dev(D))
+    h.reset([0])
+    y = h.scan_chunk(0, 0, *(to_dev(a[:L]) for a in (x, dt, B, C)), workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.scan(x[:L], dt[:L], B[:L], C[:L], A, D)
+    assert_close(host(y), ref["y"], what="y", **F32_TOL)
+    assert_close(host(h.state[0]), ref["state"], what="state", **F32_TOL)
+    st = ref["state"][None].copy()
+    pos = np.array([L], np.int64)
+    for t in range(L, L + 4):
+        yd = h.decode_step([0], *(to_dev(a[t:t + 1]) for a in (x, dt, B, C)))
+        yr = oracle.decode(st, pos, np.zeros(1, np.int64), x[t:t + 1], dt[t:t + 1], B[t:t + 1],
+                           C[t:t + 1], A, D)
+        torch.cuda.synchronize()
+        assert_close(host(yd), yr, what=f"decode {t}", **F32_TOL)
+    assert_close(host(h.state[0]), st[0], what="state after decode", **F32_TOL)
+    h.destroy()
+
+
 def test_mfma_form_negative_dt(ssm):
     """A finite negative dt is accepted (the pages give no rule against it):
     the head-pair kernel carries |dt| in the mask's exponent and takes the
