@@ -22,16 +22,17 @@ def ssm():
     return m
 
 
-@pytest.mark.parametrize("W,n_in,H,P,N,G,io", [
-    (8, 5, 2, 8, 16, 1, "f32"),
-    (16, 5, 3, 40, 20, 1, "f32"),
-    (32, 5, 4, 72, 128, 2, "f32"),
-    (8, 1, 2, 64, 128, 1, "f32"),   # one token per step: the plain-decode case
-    (16, 5, 2, 64, 128, 1, "bf16"),
-    (5, 5, 2, 16, 32, 1, "f32"),    # every step flushes a full window
-    (64, 16, 2, 64, 128, 1, "f32"),  # the largest window and in-flight count (>64 KiB LDS)
+@pytest.mark.parametrize("W,n_in,H,P,N,G,io,neg", [
+    (8, 5, 2, 8, 16, 1, "f32", False),
+    (16, 5, 3, 40, 20, 1, "f32", False),
+    (32, 5, 4, 72, 128, 2, "f32", False),
+    (8, 1, 2, 64, 128, 1, "f32", False),   # one token per step: the plain-decode case
+    (16, 5, 2, 64, 128, 1, "bf16", False),
+    (5, 5, 2, 16, 32, 1, "f32", False),    # every step flushes a full window
+    (64, 16, 2, 64, 128, 1, "f32", False),  # the largest window and in-flight count (>64 KiB LDS)
+    (8, 5, 2, 64, 128, 1, "f32", True),    # some dt negative (accepted input)
 ])
-def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io):
+def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, neg):
     S, b, steps = 6, 4, 40
     say("replay small", W, n_in, H, P, N, G, io)
     A, D = inputs.params(40, H)
@@ -51,6 +52,9 @@ def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io):
     for s in range(steps):
         x, dt, B, C = inputs.spec_step_inputs(s, batch=b, n_in=n_in, H=H, P=P, N=N, G=G,
                                               workload=40)
+        if neg:
+            dt = dt.copy()
+            dt[:, s % n_in, s % H] = -0.02
         if io == "bf16":
             bits = [inputs.bf16_bits(a) for a in (x, dt, B, C)]
             x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
