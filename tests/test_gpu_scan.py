@@ -204,10 +204,12 @@ def test_fp32_forms_negative_dt(ssm, ws):
     h.destroy()
 
 
-def test_mfma_form_negative_dt(ssm):
+@pytest.mark.parametrize("one_head", [False, True])
+def test_mfma_form_negative_dt(ssm, one_head):
     """A finite negative dt is accepted (the pages give no rule against it):
     the head-pair kernel carries |dt| in the mask's exponent and takes the
-    sign from dt itself.  Negative runs in one head only, in both heads, and
+    sign from dt itself; the one-head kernel (dt behind a one-element offset)
+    multiplies by dt.  Negative runs in one head only, in both heads, and
     across a block boundary, with a reset and checkpoints."""
     H, P, N, G, L = 4, 64, 128, 1, 300
     say("scan negative dt", H, L)
@@ -222,6 +224,11 @@ def test_mfma_form_negative_dt(ssm):
     x, dt, B, C = [inputs.bf16_to_f32(a) for a in bits]
     assert (dt < 0).sum() == 5 + 20 + 4 + 4
     dev = [bf16_dev(a) for a in bits]
+    if one_head:  # the same dt values, 2-byte but not 4-byte aligned
+        padded = torch.zeros(L * H + 1, dtype=torch.bfloat16, device="cuda")
+        padded[1:] = dev[1].reshape(-1)
+        dev[1] = padded[1:].view(L, H)
+        assert dev[1].data_ptr() % 4 == 2
     reset = np.zeros(L, np.uint8)
     reset[200] = 1
     ck = [14, 69, 130, 199, 203, 299]
