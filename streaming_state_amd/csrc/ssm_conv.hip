@@ -95,7 +95,7 @@ template <typename T> struct Raw<T, 1> {
 };
 // Tokens per thread in the chunk kernel: all of a thread's inputs (its tokens
 // and the K-1 before them) are loaded before any output is stored.
-constexpr int kConvRun = 16;
+constexpr int kConvRun = 32;
 
 // Grid (channel groups of blockDim.x * V, token runs of kConvRun).  The K-1
 // window entries before the run are held as fp32 (they may come from the
