@@ -162,6 +162,9 @@ def main():
               "share is the workload measured here)",
               file=sys.stderr)
         sys.exit(2)
+    # child processes that use the GPU run before this process initialises it
+    devinfo = device_info()
+    abi_lat = None if (args.skip_extras or args.only) else abi_latency()
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -230,10 +233,13 @@ def main():
         d4 = inputs.device_prefill(L4, H, P, N, G)
         lengths = inputs.sequence_lengths()
         reset4, cu4, ends4 = inputs.packed_layout(lengths)
-        pre = ssm.StreamState(H, P, N, 1, d4["A"], d4["D"], G=G, io_dtype="bf16")
-        pre.reset([0])
+        nseq4 = len(lengths)
+        pre = ssm.StreamState(H, P, N, nseq4, d4["A"], d4["D"], G=G, io_dtype="bf16")
+        pre.reset(list(range(nseq4)))
+        slots4 = np.arange(nseq4, dtype=np.int32)
+        cu4 = cu4.astype(np.int32)
         y4 = torch.empty((L4, H, P), dtype=torch.bfloat16, device=dev)
-        ck4 = torch.empty((len(ends4), H, P, N), dtype=torch.float32, device=dev)
+        ck4 = torch.empty((nseq4, H, P, N), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log("setup done")
 
@@ -241,7 +247,6 @@ def main():
     y_dec = torch.empty((Bd, H, P), dtype=torch.float32, device=dev)
     y_spec = torch.empty((Bd, n_in, H, P), dtype=torch.float32, device=dev)
     step_bytes, step_state_bytes = [], []
-    pre_seq = [0]
     flushes_before = 0
 
     rep_bytes, rep_bytes_all = [], []
@@ -290,9 +295,9 @@ def main():
             cop.copy_commit(slots3, a)
         if pre is not None:
             e = t_pre.start() if timed else None
-            pre.scan_chunk(0, pre_seq[0], d4["x"], d4["dt"], d4["B"], d4["C"], y=y4,
-                           reset=reset4, ckpt_at=ends4, ckpt_out=ck4)
-            pre_seq[0] += 1
+            # each sequence starts a fresh stream in its own slot; final states
+            # land there and, as checkpoints, in ck4
+            pre.scan_packed(cu4, slots4, d4["x"], d4["dt"], d4["B"], d4["C"], y=y4, final=ck4)
             if timed:
                 t_pre.stop(e)
 
@@ -313,20 +318,22 @@ def main():
     comp = {}
     if want("decode"):
         ms = np.array(t_dec.ms())
-        gbps = np.array(step_bytes) / (ms * 1e-3) / 1e9
-        state_gbps = np.array(step_state_bytes) / (ms * 1e-3) / 1e9
+        # whole-run rate: every timed step's bytes over every timed step's time
+        gbps = float(np.sum(step_bytes) / (ms.sum() * 1e-3) / 1e9)
+        state_gbps = float(np.sum(step_state_bytes) / (ms.sum() * 1e-3) / 1e9)
         comp["decode"] = dict(ms_mean=float(ms.mean()), ms_median=float(np.median(ms)),
-                              GBps=float(gbps.mean()), state_GBps=float(state_gbps.mean()),
-                              frac_hbm=float(gbps.mean() / HBM_PEAK_GBPS),
+                              GBps=gbps, state_GBps=state_gbps,
+                              frac_hbm=gbps / HBM_PEAK_GBPS,
                               bytes_per_step=float(np.mean(step_bytes)))
     if rep16 is not None:
         ms = np.array(t_rep.ms())
+        rate = float(np.sum(rep_bytes) / (ms.sum() * 1e-3))
         comp["replay_W16"] = dict(ms_mean=float(ms.mean()), ms_median=float(np.median(ms)),
                                   flushes=int(rep16.counters()["replay_flushes"] - flushes_before),
                                   bytes_per_step=float(np.mean(rep_bytes)),
-                                  GBps=float(np.mean(rep_bytes) / (ms.mean() * 1e-3) / 1e9),
+                                  GBps=rate / 1e9,
                                   bytes_each_step_with_warmup=[int(b) for b in rep_bytes_all],
-                                  frac_hbm=float(np.mean(rep_bytes) / (ms.mean() * 1e-3) / 8e12),
+                                  frac_hbm=rate / 8e12,
                                   traffic_over_algorithmic_counters=replay_counter_traffic())
     if cop is not None:
         ms = np.array(t_cop.ms())
@@ -359,18 +366,26 @@ def main():
         for W in (8, 32):
             r = make_replay(W)
             tm = Timer(torch)
-            nst = 48
-            for s in range(nst + 4):
+            nst, warm = 48, 4
+            wbytes = []
+            for s in range(nst + warm):
                 sp = spec_in[s % len(spec_in)]
-                e = tm.start() if s >= 4 else None
+                if s >= warm:
+                    wbytes.append(replay_bytes(r, slots3, W))
+                e = tm.start() if s >= warm else None
                 r.replay_step(slots3, *sp, y=y_spec)
-                if s >= 4:
+                if s >= warm:
                     tm.stop(e)
                 r.replay_commit(slots3, acc_all[s])
             torch.cuda.synchronize()
-            ms = float(np.mean(tm.ms()))
-            extras[f"replay_W{W}"] = dict(ms_mean=ms, flushes=r.counters()["replay_flushes"],
-                                          steps=nst + 4)
+            wms = np.array(tm.ms())
+            ms = float(wms.mean())
+            rate = float(np.sum(wbytes) / (wms.sum() * 1e-3))
+            extras[f"replay_W{W}"] = dict(ms_mean=ms, ms_median=float(np.median(wms)),
+                                          flushes=r.counters()["replay_flushes"],
+                                          steps=nst + warm, timed_steps=nst,
+                                          bytes_per_step=float(np.mean(wbytes)),
+                                          GBps=rate / 1e9, frac_hbm=rate / 8e12)
             if cop is not None:
                 extras[f"replay_vs_copy_speedup_W{W}"] = comp["copy"]["ms_mean"] / ms
             r.destroy()
@@ -408,6 +423,8 @@ def main():
                                        us_per_call=gpu_ms * 1e3 / len(sizes),
                                        host_wall_us_per_call=wall1 * 1e6 / len(sizes))
         extras["stream_130m"] = stream1
+        # the same calls through the C ABI with no binding in the loop
+        extras["stream_130m_abi"] = abi_lat
         extras["replay_alone_vs_decode"] = replay_alone_sweep(torch, ssm, inputs, H, P, N, G, dev)
         extras["conv_and_gate"] = conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev)
         # plain device copy of 1 GiB for the achievable-bandwidth context
@@ -465,9 +482,52 @@ def main():
                      "traffic_over_algorithmic": traffic_ratio},
         "cpu_baseline": cpu,
         "extras": extras,
-        "device": torch.cuda.get_device_name(0),
+        "device": dict(devinfo, name=torch.cuda.get_device_name(0),
+                       arch=getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+                       torch_multiprocessors=torch.cuda.get_device_properties(0).multi_processor_count),
     }
     print(json.dumps(line), flush=True)
+
+
+def device_info():
+    """Compute units and peak engine clock of the first GPU agent, as rocminfo
+    reports them (the denominators of the roofline fractions assume 256 CUs at
+    2.4 GHz)."""
+    import subprocess
+    info = {"compute_units": None, "max_clock_mhz": None, "agent": None}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return info
+    for block in out.split("*******"):
+        if "Device Type:" in block and "GPU" in block.split("Device Type:", 1)[1][:40]:
+            for ln in block.splitlines():
+                ln = ln.strip()
+                if ln.startswith("Name:") and info["agent"] is None:
+                    info["agent"] = ln.split(":", 1)[1].strip()
+                elif ln.startswith("Compute Unit:"):
+                    info["compute_units"] = int(ln.split(":", 1)[1])
+                elif ln.startswith("Max Clock Freq. (MHz):"):
+                    info["max_clock_mhz"] = int(ln.split(":", 1)[1])
+            break
+    return info
+
+
+def abi_latency():
+    """Run the C-ABI latency probe (ssm_abi_latency) as a child process: per
+    call of ssm_scan_chunk on the Mamba-130M-shaped layer, host time inside
+    the call, host wall time to completion and device time."""
+    import subprocess
+    exe = os.path.join(ROOT, "streaming_state_amd", "ssm_abi_latency")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    except subprocess.SubprocessError as e:
+        return {"error": str(e)}
+    if r.returncode != 0:
+        return {"error": r.stderr.strip()[-500:]}
+    return json.loads(r.stdout)
 
 
 def conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev, reps=10):

@@ -29,8 +29,9 @@
  *  - Ownership.  The caller allocates and frees every device buffer (state,
  *    inputs, outputs, replay log, copy buffer, workspace, checkpoints).  The
  *    library never frees them.  It owns its host metadata and, per handle, one
- *    small device buffer (checksum and finite-check flags, 4 KiB) allocated on
- *    first use and freed by ssm_destroy.
+ *    small device buffer (checksum and finite-check flags, 4 KiB) taken on
+ *    first use from a per-device pool the library keeps until the process
+ *    ends; ssm_destroy returns it to the pool.
  *  - Pointers named d_* or documented "device" are device pointers; h_* are
  *    host pointers read before the call returns.  x, dt, B, C, y use the
  *    handle's io dtype; state, checkpoints, A and D are fp32.
@@ -128,12 +129,24 @@ typedef int64_t ssm_handle;
  * parameters (device, kept by pointer: they must outlive the handle).  Every
  * slot starts as a fresh stream at position 0 with chunk_seq 0; the caller
  * decides what d_state holds (ssm_state_reset / ssm_state_init write it).
- * flags: SSM_FLAG_*.  No device call is made. */
+ * A slot is the stream-owned record of one stream's state, position and
+ * chunk sequence ("Mamba Streaming State That Survives Chunking", section
+ * "Treat Mamba streaming state as a stream-owned record"); the state is one
+ * fixed-size fp32 array per stream and layer ("Why Speculative Decoding Slows
+ * Hybrid Mamba Models at Large Batch Sizes", section "The Problem").
+ * flags: SSM_FLAG_*.  No device call is made.  Errors: SSM_E_INVALID_ARG for
+ * a bad desc, n_slots < 1, a NULL or misaligned (16 bytes) state, NULL A/D,
+ * or unknown flags. */
 ssm_status ssm_create(const ssm_layer_desc *desc, int32_t n_slots, float *d_state,
                       const float *d_A, const float *d_D, uint32_t flags, ssm_handle *out);
 
-/* Cancel: release the handle.  Work already enqueued still completes; any later
- * call with this handle returns SSM_E_INVALID_STATE. */
+/* Cancel: release the handle (cancellation must be observable: "Mamba
+ * Streaming State That Survives Chunking", section "Make reset, checkpoint,
+ * and cancellation observable").  Work already enqueued still completes.
+ * Nothing is synchronised: every call that uses the handle's scratch buffer
+ * has synchronised its stream before returning, so the buffer goes back to
+ * the library's pool at once.  Any later call with this handle returns
+ * SSM_E_INVALID_STATE. */
 ssm_status ssm_destroy(ssm_handle h);
 
 /* Reset h_slots[n] (distinct): state zeroed on `stream`, position 0, chunk_seq
@@ -189,6 +202,42 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
                           const int64_t *h_ckpt_at, float *d_ckpt_out, void *d_workspace,
                           size_t ws_bytes, void *stream);
 
+/* Scan a batch of packed sequences, each into its own slot: the prefill of
+ * several streams in one call.  Sequence i holds tokens [h_cu_seqlens[i],
+ * h_cu_seqlens[i+1]) of x[L,H,P] dt[L,H] B,C[L,G,N] (device, io dtype;
+ * L = h_cu_seqlens[nseq]) and writes y[L,H,P].  Its final state becomes the
+ * state of slot h_seq_slots[i] (host, distinct) together with its position,
+ * so that decode continues each stream where its prefill ended (continuous
+ * batching moves recurrent state and position together: "Mamba Streaming
+ * State That Survives Chunking", section "Separate Mamba-2 algebra from
+ * kernel behavior").
+ *   h_cu_seqlens  host int32[nseq+1]: 0 first, non-decreasing (empty
+ *                 sequences are legal)
+ *   h_continue    host u8[nseq] or NULL.  0 (or NULL): the sequence starts a
+ *                 new stream from a zero state (a reset on its first token);
+ *                 the slot gets a new stream id, position = its length and
+ *                 chunk_seq 1.  Nonzero: it continues the slot's stream from
+ *                 the slot's state; h_chunk_seq[i] must equal the slot's next
+ *                 chunk sequence number (else SSM_E_SEQUENCE, nothing
+ *                 changed), and position and chunk_seq advance as for
+ *                 ssm_scan_chunk.
+ *   h_chunk_seq   host u64[nseq]; required when any h_continue is set
+ *   d_final       device fp32 [nseq,H,P,N] or NULL: a copy of every
+ *                 sequence's final state (the checkpoint of each sequence)
+ *   h_receipts    host [nseq] or NULL: the receipt of each slot's new state
+ *                 (section "Make reset, checkpoint, and cancellation
+ *                 observable": stream id, position, chunk sequence,
+ *                 checksum...); with d_final, d_final[i] and h_receipts[i]
+ *                 restore the stream into any slot (ssm_state_restore).
+ *                 Taking the checksums synchronises `stream`.
+ * Every slot must have no pending replay log or live copy (SSM_E_LOG).  No
+ * workspace is needed: distinct slots never share a state. */
+ssm_status ssm_scan_packed(ssm_handle h, int32_t nseq, const int32_t *h_cu_seqlens,
+                           const int32_t *h_seq_slots, const uint8_t *h_continue,
+                           const uint64_t *h_chunk_seq, const void *x, const void *dt,
+                           const void *B, const void *C, void *y, float *d_final,
+                           ssm_receipt *h_receipts, void *stream);
+
 /* ------------------------------------------------------------------ decode */
 
 /* One token for each of `batch` distinct slots h_slot_ids[batch] (decode moves
@@ -229,7 +278,11 @@ ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
 
 /* Commit the last replay step of each slot: h_accepted[i] (1..n_in) leading
  * in-flight tokens join the log and the position; the rest are dropped (they
- * never enter the committed log).  Host only. */
+ * never enter the committed log: "Why Speculative Decoding Slows Hybrid Mamba
+ * Models at Large Batch Sizes", section "The Fix: Log the Inputs, Checkpoint
+ * the State"; the accepted count is the real token plus the drafts before
+ * the first miss, section "Implementing It").  Host only: SSM_E_LOG for a
+ * slot with no replay step awaiting commit or a count outside [1, n_in]. */
 ssm_status ssm_replay_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
                              const int32_t *h_accepted);
 
@@ -262,15 +315,26 @@ ssm_status ssm_copy_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_id
 ssm_status ssm_state_materialize(ssm_handle h, int32_t n, const int32_t *h_slots, void *stream);
 
 /* Checkpoint `slot`: materialize it, copy its state to d_dst[H,P,N] (device
- * fp32) and fill *out.  Synchronises `stream` (the checksum is computed on the
- * device and read back). */
+ * fp32) and fill *out with the receipt a resume needs ("Mamba Streaming State
+ * That Survives Chunking", section "Make reset, checkpoint, and cancellation
+ * observable": stream id, revisions, schema, dtype, dimensions, absolute
+ * position, chunk sequence and checksum).  In a replay stream the checkpoint
+ * is the whole state after folding the log ("Why Speculative Decoding Slows
+ * Hybrid Mamba Models at Large Batch Sizes", Glossary).  Synchronises
+ * `stream` (the checksum is computed on the device and read back).  Errors:
+ * SSM_E_INVALID_ARG (bad slot, NULL or misaligned d_dst, NULL out), SSM_E_LOG
+ * (a verify step awaits commit). */
 ssm_status ssm_state_checkpoint(ssm_handle h, int32_t slot, float *d_dst, ssm_receipt *out,
                                 void *stream);
 
 /* Resume `slot` from d_src[H,P,N] and its receipt.  Any semantic mismatch
  * (schema version, dtype, H, P, N, G, model or code revision) or a checksum
- * that does not match d_src returns SSM_E_SCHEMA with nothing changed (reject,
- * never pad or truncate).  Synchronises `stream`. */
+ * that does not match d_src returns SSM_E_SCHEMA with nothing changed (an
+ * incompatible resume is refused, never padded or truncated: "Mamba
+ * Streaming State That Survives Chunking", sections "Make reset, checkpoint,
+ * and cancellation observable" and "Version state semantics for Mamba-3").
+ * The slot takes the receipt's stream id, position and chunk sequence.
+ * Synchronises `stream`. */
 ssm_status ssm_state_restore(ssm_handle h, int32_t slot, const float *d_src,
                              const ssm_receipt *r, void *stream);
 
@@ -364,7 +428,11 @@ ssm_status ssm_conv_decode(ssm_handle h, int32_t batch, const int32_t *h_slot_id
 ssm_status ssm_gate(int32_t io_dtype, int64_t rows, int32_t C, int32_t group, const void *y,
                     const void *z, const float *d_norm_w, float eps, void *out, void *stream);
 
-/* Read a slot's position and next expected chunk sequence number. */
+/* Read a slot's position (tokens since the stream's start or last reset, the
+ * counter of the runnable artifact in "Mamba Streaming State That Survives
+ * Chunking") and next expected chunk sequence number (section "Let the full
+ * scan define legal chunking").  Either pointer may be NULL.  SSM_E_INVALID_ARG
+ * for a bad slot. */
 ssm_status ssm_get_position(ssm_handle h, int32_t slot, int64_t *pos, uint64_t *chunk_seq);
 
 /* Read the replay log length of a slot (committed entries) and whether a

@@ -3,7 +3,8 @@
 Run ``python -m streaming_state_amd.build`` or call ``build()``.  The sources
 are the host runtime (``csrc/ssm_host.cpp``) and the kernels
 (``csrc/*.hip``); every file is compiled for gfx950 only, with packed fp32
-instructions disabled.
+instructions disabled.  ``ssm_abi_latency`` (``csrc/abi_latency.cpp``) is a
+small program that times the C ABI's scan call with no binding in the loop.
 """
 import os
 import subprocess
@@ -15,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm_stream.so")
+LATENCY = os.path.join(HERE, "ssm_abi_latency")
 SOURCES = ["ssm_host.cpp", "ssm_decode.hip", "ssm_kernels.hip", "ssm_scan.hip", "ssm_ssd.hip", "ssm_ssd_pair.hip", "ssm_chunk.hip", "ssm_conv.hip"]
 ARCH = "gfx950"
 
@@ -52,6 +54,14 @@ def build(verbose=False):
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stderr}")
         os.replace(tmp_lib, LIB)
+        # the C-ABI latency probe, linked against the library just built
+        tmp_exe = LATENCY + ".tmp%d" % os.getpid()
+        cmd = [HIPCC] + FLAGS + ["-x", "hip", os.path.join(CSRC, "abi_latency.cpp"), "-o", tmp_exe,
+               "-L", HERE, "-lssm_stream", "-Wl,-rpath,$ORIGIN"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on abi_latency.cpp:\n{r.stderr}")
+        os.replace(tmp_exe, LATENCY)
     return LIB
 
 

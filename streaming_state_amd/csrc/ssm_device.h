@@ -6,9 +6,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "ssm_internal.h"
 
 namespace ssm {
+
+// ------------------------------------------------------- launch attributes
+// Allow `kernel` `bytes` of dynamic LDS on the current device.  Above the
+// default 64 KiB the limit must be raised with hipFuncSetAttribute; it
+// persists, so it is raised once per (kernel, device, size) rather than on
+// every launch.
+inline hipError_t allow_dynamic_lds(const void *kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  struct Set {
+    const void *kernel;
+    int dev;
+    size_t bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Set> done;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lk(mu);
+  for (const Set &e : done)
+    if (e.kernel == kernel && e.dev == dev && e.bytes >= bytes) return hipSuccess;
+  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (err == hipSuccess) done.push_back(Set{kernel, dev, bytes});
+  return err;
+}
 
 // ------------------------------------------------------------------ io types
 // fp32 is stored as float, bf16 as its 16-bit pattern.

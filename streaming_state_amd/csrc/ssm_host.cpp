@@ -72,8 +72,9 @@ struct Handle {
   int conv_C = 0, conv_K = 0, conv_act = 0;
   float *conv_state = nullptr;  // [S, C, K-1]
   const float *conv_w = nullptr, *conv_b = nullptr;
-  // device scratch: [0] checksum accumulator (u64), [1] finite flag (u32)
+  // device scratch slice (checksum accumulators, finite flag) and its device
   void *scratch = nullptr;
+  int scratch_dev = 0;
   ssm_counters cnt{};
   size_t state_bytes() const { return (size_t)d.H * d.P * d.N * sizeof(float); }
   float *slot_state(int s) const { return state + (size_t)s * d.H * d.P * d.N; }
@@ -163,10 +164,46 @@ ssm_status check_slots(Handle *H, int n, const int32_t *slots, const char *what)
   return SSM_OK;
 }
 
+// Per-handle device scratch: kSums checksum accumulators (u64), then the
+// finite-check flag.
+constexpr size_t kScratchBytes = 4096;
+constexpr int kSums = 256;
+constexpr size_t kFlagOff = kSums * sizeof(unsigned long long);
+static_assert(kFlagOff + sizeof(unsigned int) <= kScratchBytes, "scratch layout");
+
+// Scratch slices come from a per-device pool that is never freed: every call
+// that uses a handle's slice synchronises its stream before it returns, so a
+// slice returned by ssm_destroy is idle and can serve the next handle without
+// any device-wide wait (hipFree would synchronise the whole device).
+constexpr int kSlicesPerBlock = 64;
+struct ScratchPool {
+  std::mutex mu;
+  std::unordered_map<int, std::vector<void *>> free_slices;  // by device
+};
+ScratchPool g_pool;
+
 ssm_status ensure_scratch(Handle *H) {
   if (H->scratch) return SSM_OK;
-  HIP_TRY(hipMalloc(&H->scratch, 4096));
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_pool.mu);
+  std::vector<void *> &fl = g_pool.free_slices[dev];
+  if (fl.empty()) {
+    char *block = nullptr;
+    HIP_TRY(hipMalloc((void **)&block, kScratchBytes * kSlicesPerBlock));
+    for (int i = kSlicesPerBlock - 1; i >= 0; --i) fl.push_back(block + i * kScratchBytes);
+  }
+  H->scratch = fl.back();
+  H->scratch_dev = dev;
+  fl.pop_back();
   return SSM_OK;
+}
+
+void release_scratch(Handle *H) {
+  if (!H->scratch) return;
+  std::lock_guard<std::mutex> lk(g_pool.mu);
+  g_pool.free_slices[H->scratch_dev].push_back(H->scratch);
+  H->scratch = nullptr;
 }
 
 // Device-side finite check of a list of io-dtype buffers; synchronises.
@@ -174,7 +211,7 @@ ssm_status check_finite(Handle *H, hipStream_t s, std::initializer_list<std::pai
   if (!(H->flags & SSM_FLAG_CHECK_FINITE)) return SSM_OK;
   ssm_status st = ensure_scratch(H);
   if (st != SSM_OK) return st;
-  unsigned int *flag = reinterpret_cast<unsigned int *>((char *)H->scratch + 64);
+  unsigned int *flag = reinterpret_cast<unsigned int *>((char *)H->scratch + kFlagOff);
   HIP_TRY(launch_zero_u64(reinterpret_cast<unsigned long long *>(flag), 1, s));
   for (auto &b : bufs) HIP_TRY(launch_finite_check(H->io, b.first, b.second, flag, s));
   unsigned int host = 0;
@@ -184,18 +221,32 @@ ssm_status check_finite(Handle *H, hipStream_t s, std::initializer_list<std::pai
   return SSM_OK;
 }
 
-ssm_status device_checksum(Handle *H, const float *src, hipStream_t s, uint64_t *out) {
+// Receipt checksums of n states srcs[i] (each [H,P,N] fp32, device), taken on
+// the device in batches of kSums; synchronises the stream.
+ssm_status device_checksums(Handle *H, const float *const *srcs, int n, hipStream_t s,
+                            uint64_t *out) {
   ssm_status st = ensure_scratch(H);
   if (st != SSM_OK) return st;
   unsigned long long *acc = reinterpret_cast<unsigned long long *>(H->scratch);
-  HIP_TRY(launch_zero_u64(acc, 1, s));
-  HIP_TRY(launch_checksum(src, H->state_bytes() / 4, acc, s));
-  unsigned long long host = 0;
-  HIP_TRY(hipMemcpyAsync(&host, acc, sizeof host, hipMemcpyDeviceToHost, s));
-  HIP_TRY(hipStreamSynchronize(s));
-  *out = host;
+  unsigned long long host[kSums];
+  for (int i0 = 0; i0 < n; i0 += kSums) {
+    const int k = std::min(kSums, n - i0);
+    HIP_TRY(launch_zero_u64(acc, k, s));
+    for (int i = 0; i < k; ++i)
+      HIP_TRY(launch_checksum(srcs[i0 + i], H->state_bytes() / 4, acc + i, s));
+    HIP_TRY(hipMemcpyAsync(host, acc, k * sizeof(unsigned long long), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    for (int i = 0; i < k; ++i) out[i0 + i] = host[i];
+  }
   return SSM_OK;
 }
+
+ssm_status device_checksum(Handle *H, const float *src, hipStream_t s, uint64_t *out) {
+  return device_checksums(H, &src, 1, s, out);
+}
+
+// The receipt of a slot's current stream for a state whose checksum is `sum`.
+ssm_receipt slot_receipt(const Handle *H, const Slot &sl, uint64_t sum);
 
 ssm_status slot_is_plain(Handle *H, int s, const char *what) {
   const Slot &sl = H->slots[s];
@@ -278,6 +329,72 @@ ssm_status materialize(Handle *H, int n, const int32_t *slots, hipStream_t s) {
   return SSM_OK;
 }
 
+ssm_receipt slot_receipt(const Handle *H, const Slot &sl, uint64_t sum) {
+  ssm_receipt r{};
+  r.stream_id = sl.stream_id;
+  r.model_rev = H->desc.model_rev;
+  r.code_rev = kCodeRev;
+  r.schema_version = H->desc.schema_version;
+  r.state_dtype = SSM_F32;
+  r.H = H->d.H;
+  r.P = H->d.P;
+  r.N = H->d.N;
+  r.G = H->d.G;
+  r.position = sl.pos;
+  r.chunk_seq = sl.chunk_seq;
+  r.checksum = sum;
+  return r;
+}
+
+// Launch the per-segment forms of the scan over `segs` (in token order): the
+// head-pair or one-head SSD kernel for bf16 with P = 64, N = 128, the
+// recurrent kernel otherwise.  Segment i starts from state[segs[i].slot] (or
+// zero) and ends in it (or the workspace, or nowhere: see ScanSeg).  The
+// state right after token ck_at[i] goes to ckpt_out[i].
+ssm_status launch_seg_forms(Handle *H, float *state, float *ws, const std::vector<ScanSeg> &segs,
+                            const void *x, const void *dt, const void *B, const void *C, void *y,
+                            int n_ckpt, const int64_t *ck_at, float *ckpt_out, hipStream_t s) {
+  const bool ssd = ssd_supported(H->io, H->d);
+  for (size_t i0 = 0; i0 < segs.size(); i0 += kSegPerLaunch) {
+    const int ns = (int)std::min<size_t>(kSegPerLaunch, segs.size() - i0);
+    ScanMeta m{};
+    for (int i = 0; i < ns; ++i) m.seg[i] = segs[i0 + i];
+    if (ssd)  // longest segments first: one workgroup per (segment, head) runs it in order
+      std::stable_sort(m.seg, m.seg + ns, [](const ScanSeg &a, const ScanSeg &b) {
+        return a.t1 - a.t0 > b.t1 - b.t0;
+      });
+    const int32_t lo = segs[i0].t0, hi = segs[i0 + ns - 1].t1;
+    int nck = 0;
+    for (int i = 0; i < n_ckpt; ++i)
+      if (ck_at[i] >= lo && ck_at[i] < hi) {
+        m.ck_t[nck] = (int32_t)ck_at[i];
+        m.ck_idx[nck] = i;
+        ++nck;
+      }
+    ScanArgs a{};
+    a.x = x;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.y = y;
+    a.state = state;
+    a.workspace = ws;
+    a.ckpt_out = ckpt_out;
+    a.A = H->A;
+    a.D = H->D;
+    a.d = H->d;
+    a.n_seg = ns;
+    a.n_ck = nck;
+    if (ssd && ssd_pair_supported(a))
+      HIP_TRY(launch_scan_ssd_pair(a, m, s));
+    else if (ssd)
+      HIP_TRY(launch_scan_ssd(a, m, s));
+    else
+      HIP_TRY(launch_scan(H->io, a, m, s));
+  }
+  return SSM_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -326,11 +443,7 @@ ssm_status ssm_destroy(ssm_handle h) {
     H = it->second;
     g_handles.erase(it);
   }
-  if (H->scratch) {
-    // work already enqueued may still use the scratch buffer
-    (void)hipDeviceSynchronize();
-    (void)hipFree(H->scratch);
-  }
+  release_scratch(H);  // idle: its last user synchronised its stream
   delete H;
   return SSM_OK;
 }
@@ -472,7 +585,7 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
     const bool first_init = !(h_reset && h_reset[0]);
     for (int64_t t = 1; t <= L; ++t) {
       if (t == L || (h_reset && h_reset[t])) {
-        segs.push_back(ScanSeg{t0, (int32_t)t, (int32_t)(segs.empty() ? first_init : 0), 0});
+        segs.push_back(ScanSeg{t0, (int32_t)t, (int32_t)(segs.empty() ? first_init : 0), 0, 0});
         t0 = (int32_t)t;
       }
     }
@@ -489,42 +602,10 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
                              {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
     if (st != SSM_OK) return st;
   }
-  for (size_t i0 = 0; !par && i0 < segs.size(); i0 += kSegPerLaunch) {
-    const int ns = (int)std::min<size_t>(kSegPerLaunch, segs.size() - i0);
-    ScanMeta m{};
-    for (int i = 0; i < ns; ++i) m.seg[i] = segs[i0 + i];
-    if (ssd)  // longest segments first: one workgroup per (segment, head) runs it in order
-      std::stable_sort(m.seg, m.seg + ns, [](const ScanSeg &a, const ScanSeg &b) {
-        return a.t1 - a.t0 > b.t1 - b.t0;
-      });
-    const int32_t lo = segs[i0].t0, hi = segs[i0 + ns - 1].t1;
-    int nck = 0;
-    for (int i = 0; i < n_ckpt; ++i)
-      if (h_ckpt_at[i] >= lo && h_ckpt_at[i] < hi) {
-        m.ck_t[nck] = (int32_t)h_ckpt_at[i];
-        m.ck_idx[nck] = i;
-        ++nck;
-      }
-    ScanArgs a{};
-    a.x = x;
-    a.dt = dt;
-    a.B = B;
-    a.C = C;
-    a.y = y;
-    a.state = H->slot_state(slot);
-    a.workspace = (float *)d_workspace;
-    a.ckpt_out = d_ckpt_out;
-    a.A = H->A;
-    a.D = H->D;
-    a.d = H->d;
-    a.n_seg = ns;
-    a.n_ck = nck;
-    if (ssd && ssd_pair_supported(a))
-      HIP_TRY(launch_scan_ssd_pair(a, m, s));
-    else if (ssd)
-      HIP_TRY(launch_scan_ssd(a, m, s));
-    else
-      HIP_TRY(launch_scan(H->io, a, m, s));
+  if (!par) {
+    st = launch_seg_forms(H, H->slot_state(slot), (float *)d_workspace, segs, x, dt, B, C, y,
+                          n_ckpt, h_ckpt_at, d_ckpt_out, s);
+    if (st != SSM_OK) return st;
   }
   if (need_ws)
     HIP_TRY(launch_copy_f32(H->slot_state(slot), (const float *)d_workspace,
@@ -541,6 +622,115 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
   H->cnt.tokens_scanned += (uint64_t)L;
   if (segs.front().init) H->cnt.state_bytes_read += H->state_bytes();
   H->cnt.state_bytes_written += H->state_bytes() * (1 + (size_t)n_ckpt);
+  return SSM_OK;
+}
+
+ssm_status ssm_scan_packed(ssm_handle h, int32_t nseq, const int32_t *h_cu_seqlens,
+                           const int32_t *h_seq_slots, const uint8_t *h_continue,
+                           const uint64_t *h_chunk_seq, const void *x, const void *dt,
+                           const void *B, const void *C, void *y, float *d_final,
+                           ssm_receipt *h_receipts, void *stream) {
+  GET_HANDLE(H, h);
+  if (nseq < 0) return fail(SSM_E_INVALID_ARG, "scan packed: negative sequence count");
+  if (nseq == 0) return SSM_OK;
+  if (!h_cu_seqlens) return fail(SSM_E_INVALID_ARG, "scan packed: cu_seqlens is NULL");
+  if (h_cu_seqlens[0] != 0) return fail(SSM_E_INVALID_ARG, "scan packed: cu_seqlens[0] must be 0");
+  for (int i = 0; i < nseq; ++i)
+    if (h_cu_seqlens[i + 1] < h_cu_seqlens[i])
+      return fail(SSM_E_INVALID_ARG, "scan packed: cu_seqlens decreases at %d", i + 1);
+  ssm_status st = check_slots(H, nseq, h_seq_slots, "scan packed");
+  if (st != SSM_OK) return st;
+  for (int i = 0; i < nseq; ++i) {
+    st = slot_is_plain(H, h_seq_slots[i], "scan packed");
+    if (st != SSM_OK) return st;
+  }
+  bool any_cont = false;
+  for (int i = 0; i < nseq; ++i) any_cont |= h_continue && h_continue[i];
+  if (any_cont && !h_chunk_seq)
+    return fail(SSM_E_INVALID_ARG, "scan packed: continuing sequences need h_chunk_seq");
+  for (int i = 0; i < nseq; ++i) {
+    if (!(h_continue && h_continue[i])) continue;
+    const Slot &sl = H->slots[h_seq_slots[i]];
+    if (h_chunk_seq[i] != sl.chunk_seq) {
+      H->cnt.chunks_rejected++;
+      return fail(SSM_E_SEQUENCE, "scan packed: slot %d expects chunk %llu, got %llu (%s)",
+                  h_seq_slots[i], (unsigned long long)sl.chunk_seq,
+                  (unsigned long long)h_chunk_seq[i],
+                  h_chunk_seq[i] < sl.chunk_seq ? "duplicate" : "reordered or gap");
+    }
+  }
+  const int64_t L = h_cu_seqlens[nseq];
+  if (L > 0) {
+    if (!x || !dt || !B || !C || !y)
+      return fail(SSM_E_INVALID_ARG, "scan packed: NULL input or output");
+    st = check_io_align(H->io, x, dt, B, C, y, "scan packed");
+    if (st != SSM_OK) return st;
+    if (ssd_supported(H->io, H->d) && (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16)))
+      return fail(SSM_E_INVALID_ARG, "scan packed: bf16 x, B and C must be 16-byte aligned");
+  }
+  if (d_final && !aligned(d_final, 16))
+    return fail(SSM_E_INVALID_ARG, "scan packed: d_final must be 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  if (L > 0) {
+    st = check_finite(H, s, {{x, (size_t)L * H->d.H * H->d.P}, {dt, (size_t)L * H->d.H},
+                             {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
+    if (st != SSM_OK) return st;
+  }
+  // every sequence is one segment writing its own slot; slots are distinct, so
+  // no segment reads a state another one writes
+  const size_t nf = H->state_bytes() / 4;
+  std::vector<ScanSeg> segs;
+  // with d_final, sequence i's last token is checkpoint i (-1: an empty
+  // sequence, which no launch's token range holds)
+  std::vector<int64_t> ck_at(d_final ? nseq : 0, -1);
+  for (int i = 0; i < nseq; ++i) {
+    const int32_t t0 = h_cu_seqlens[i], t1 = h_cu_seqlens[i + 1];
+    const int cont = h_continue && h_continue[i] ? 1 : 0;
+    float *slot_st = H->slot_state(h_seq_slots[i]);
+    if (t1 == t0) {  // an empty sequence: a fresh stream is zero, a continued one unchanged
+      if (!cont) HIP_TRY(launch_zero(slot_st, nf, s));
+      if (d_final) {
+        if (cont)
+          HIP_TRY(launch_copy_f32(d_final + (size_t)i * nf, slot_st, nf, s));
+        else
+          HIP_TRY(launch_zero(d_final + (size_t)i * nf, nf, s));
+      }
+      continue;
+    }
+    segs.push_back(ScanSeg{t0, t1, cont, 1, h_seq_slots[i]});
+    if (d_final) ck_at[i] = t1 - 1;
+  }
+  if (!segs.empty()) {
+    st = launch_seg_forms(H, H->state, nullptr, segs, x, dt, B, C, y, (int)ck_at.size(),
+                          ck_at.data(), d_final, s);
+    if (st != SSM_OK) return st;
+  }
+  for (int i = 0; i < nseq; ++i) {
+    Slot &sl = H->slots[h_seq_slots[i]];
+    const int64_t len = h_cu_seqlens[i + 1] - h_cu_seqlens[i];
+    if (h_continue && h_continue[i]) {
+      sl.pos += len;
+      sl.chunk_seq++;
+      if (len) H->cnt.state_bytes_read += H->state_bytes();
+    } else {
+      fresh_stream(sl);
+      sl.pos = len;
+      sl.chunk_seq = 1;
+      H->cnt.resets++;
+    }
+    H->cnt.chunks_admitted++;
+    H->cnt.state_bytes_written += H->state_bytes() * (d_final ? 2 : 1);
+  }
+  H->cnt.tokens_scanned += (uint64_t)L;
+  if (h_receipts) {
+    std::vector<const float *> src(nseq);
+    std::vector<uint64_t> sums(nseq);
+    for (int i = 0; i < nseq; ++i) src[i] = H->slot_state(h_seq_slots[i]);
+    st = device_checksums(H, src.data(), nseq, s, sums.data());
+    if (st != SSM_OK) return st;
+    for (int i = 0; i < nseq; ++i)
+      h_receipts[i] = slot_receipt(H, H->slots[h_seq_slots[i]], sums[i]);
+  }
   return SSM_OK;
 }
 
@@ -861,21 +1051,7 @@ ssm_status ssm_state_checkpoint(ssm_handle h, int32_t slot, float *d_dst, ssm_re
   uint64_t sum = 0;
   st = device_checksum(H, d_dst, s, &sum);
   if (st != SSM_OK) return st;
-  const Slot &sl = H->slots[slot];
-  ssm_receipt r{};
-  r.stream_id = sl.stream_id;
-  r.model_rev = H->desc.model_rev;
-  r.code_rev = kCodeRev;
-  r.schema_version = H->desc.schema_version;
-  r.state_dtype = SSM_F32;
-  r.H = H->d.H;
-  r.P = H->d.P;
-  r.N = H->d.N;
-  r.G = H->d.G;
-  r.position = sl.pos;
-  r.chunk_seq = sl.chunk_seq;
-  r.checksum = sum;
-  *out = r;
+  *out = slot_receipt(H, H->slots[slot], sum);
   H->cnt.checkpoints++;
   H->cnt.state_bytes_read += H->state_bytes();
   return SSM_OK;
@@ -1125,21 +1301,7 @@ ssm_status ssm_state_serialize(ssm_handle h, int32_t slot, void *h_blob, size_t 
   for (int i = 0; i < 5; ++i) put_u32(p + 4 * i, head[i]);
   memcpy(p + 20, host.data(), H->state_bytes());
   *written = need;
-  const Slot &sl = H->slots[slot];
-  ssm_receipt r{};
-  r.stream_id = sl.stream_id;
-  r.model_rev = H->desc.model_rev;
-  r.code_rev = kCodeRev;
-  r.schema_version = H->desc.schema_version;
-  r.state_dtype = SSM_F32;
-  r.H = H->d.H;
-  r.P = H->d.P;
-  r.N = H->d.N;
-  r.G = H->d.G;
-  r.position = sl.pos;
-  r.chunk_seq = sl.chunk_seq;
-  r.checksum = host_checksum(host.data(), nf);
-  *out = r;
+  *out = slot_receipt(H, H->slots[slot], host_checksum(host.data(), nf));
   H->cnt.checkpoints++;
   H->cnt.state_bytes_read += H->state_bytes();
   return SSM_OK;

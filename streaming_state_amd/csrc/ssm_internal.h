@@ -112,8 +112,9 @@ hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const
 // -------------------------------------------------------------------- scan
 struct ScanSeg {
   int32_t t0, t1;   // token range [t0, t1) of the chunk
-  int32_t init;     // 1: start from the state buffer; 0: from zero
-  int32_t final;    // 0: drop; 1: write the state buffer; 2: write the workspace
+  int32_t init;     // 1: start from the segment's state; 0: from zero
+  int32_t final;    // 0: drop; 1: write the segment's state; 2: write the workspace
+  int32_t slot;     // the segment's state is state + slot * H*P*N
 };
 struct ScanMeta {
   ScanSeg seg[kSegPerLaunch];
@@ -123,7 +124,7 @@ struct ScanMeta {
 struct ScanArgs {
   const void *x, *dt, *B, *C;
   void *y;
-  float *state;      // the slot's [H, P, N]
+  float *state;      // [.., H, P, N]: segment i reads/writes state[seg[i].slot]
   float *workspace;  // [H, P, N] or null
   float *ckpt_out;   // [n_ckpt, H, P, N]
   const float *A, *D;

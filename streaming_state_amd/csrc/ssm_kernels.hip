@@ -197,18 +197,21 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
 constexpr int kReplayR = 8;  // 64-row (32 KiB) tiles
 
 // LDS carve-up of the verify kernel (byte offsets; W window, n_in in-flight
-// tokens, rows = the tile's row count, es = io element size):
+// tokens, xs = the LDS stride of an entry's x rows (>= rows), rows = the
+// tile's row count, es = io element size):
 //   V [W + n_in][N] io   fold B rows, then in-flight C rows
-//   x [W + n_in][rows] io combined entries' x, then the fold entries' x
+//   x [W + n_in][xs] io  combined entries' x, then the fold entries' x
 //   dt [W], fdt [W], coef [W][n_in] (staged B.C, then the weights),
 //   lam [n_in], fw [W], flam [1], dot [n_in][rows]   (fp32)
+// Combined plus fold entries number at most W + n_in (a step that folds
+// starts its live half empty), so x never runs into dt.
 struct ReplaySmem {
   int V, x, dt, fdt, coef, lam, fw, flam, dot, total;
-  __host__ __device__ ReplaySmem(int W, int n_in, int N, int rows, int es) {
+  __host__ __device__ ReplaySmem(int W, int n_in, int N, int xs, int rows, int es) {
     auto up16 = [](int b) { return (b + 15) & ~15; };
     V = 0;
     x = up16(V + (W + n_in) * N * es);
-    dt = up16(x + (W + n_in) * rows * es);
+    dt = up16(x + (W + n_in) * xs * es);
     fdt = dt + 4 * W;
     coef = fdt + 4 * W;
     lam = coef + 4 * W * n_in;
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   T *logx = (T *)((char *)a.log + lay.x_off);
   const T *logB = (const T *)((const char *)a.log + lay.B_off);
   const T *inx = (const T *)a.x, *indt = (const T *)a.dt, *inC = (const T *)a.C;
-  const ReplaySmem L(W, n_in, N, rv, (int)sizeof(T));
+  const ReplaySmem L(W, n_in, N, xs, rv, (int)sizeof(T));
   T *s_V = (T *)(sb + L.V);  // [F + n_in][N]
   T *s_x = (T *)(sb + L.x);  // [J + F][xs]
   float *s_dt = (float *)(sb + L.dt), *s_fdt = (float *)(sb + L.fdt);
@@ -475,18 +478,16 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
 }
 
 static size_t replay_smem_bytes(int io, int W, int n_in, int N) {
-  return (size_t)ReplaySmem(W, n_in, N, 8 * kReplayR, io == kBF16 ? 2 : 4).total;
+  // xs and rows are at most the tile height, so this bounds every tile's need
+  return (size_t)ReplaySmem(W, n_in, N, 8 * kReplayR, 8 * kReplayR, io == kBF16 ? 2 : 4).total;
 }
 
 static size_t replay_bc_smem_bytes(int W, int n_in, int N) {
   return sizeof(float4) * (size_t)(W + n_in) * (N / 4 + 1);
 }
 
-// Dynamic LDS above 64 KiB needs the kernel's limit raised once.
 template <typename K> static hipError_t allow_lds(K kernel, size_t bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  return allow_dynamic_lds(reinterpret_cast<const void *>(kernel), bytes);
 }
 
 hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const LogLayout &lay,

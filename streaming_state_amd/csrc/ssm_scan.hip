@@ -45,9 +45,10 @@ __global__ __launch_bounds__(kThreads) void scan_rec_kernel(ScanArgs a, ScanMeta
   const float Ah = a.A[h], Dh = a.D[h];
   const T *x = (const T *)a.x, *dt = (const T *)a.dt, *Bp = (const T *)a.B, *Cp = (const T *)a.C;
 
+  float *seg_state = a.state + (size_t)sg.slot * d.H * PN;
   float4 hv[R];
   {
-    const float *st = a.state + (size_t)h * PN + tile_off;
+    const float *st = seg_state + (size_t)h * PN + tile_off;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const bool ok = sg.init && colok && (prow0 + tl.row(i) < d.P);
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void scan_rec_kernel(ScanArgs a, ScanMeta
   }
 
   if (sg.final) {
-    float *dst = (sg.final == 1 ? a.state : a.workspace) + (size_t)h * PN + tile_off;
+    float *dst = (sg.final == 1 ? seg_state : a.workspace) + (size_t)h * PN + tile_off;
 #pragma unroll
     for (int i = 0; i < R; ++i)
       if (colok && prow0 + tl.row(i) < d.P)

@@ -308,11 +308,12 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
   f32x16_t acc[3];
   f32x16_t *hacc = acc;
   f32x16_t &tile = acc[0], &mt = acc[2];
+  float *seg_state = a.state + (size_t)sg.slot * d.H * PN;
   bool have_h = sg.init != 0;
   acc[0] = zero16();
   acc[1] = zero16();
   if (have_h && swave) {
-    state_load(hacc, a.state + (size_t)h * PN, nt, l32, hi);
+    state_load(hacc, seg_state + (size_t)h * PN, nt, l32, hi);
     state_to_lds(hacc, sm.HT, nt, l32, hi);
   }
   int ck = 0;
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(kSsdThreads, 4) void scan_ssd_kernel(ScanArgs a, Sc
   }
 
   if (sg.final && swave)
-    state_store(hacc, (sg.final == 1 ? a.state : a.workspace) + (size_t)h * PN, nt, l32, hi);
+    state_store(hacc, (sg.final == 1 ? seg_state : a.workspace) + (size_t)h * PN, nt, l32, hi);
 }
 
 }  // namespace

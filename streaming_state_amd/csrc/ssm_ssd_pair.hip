@@ -596,9 +596,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void scan_ssd_pair_kernel(ScanArgs
   // ---- state in
   const size_t PN = (size_t)SP * SN;
   const int hh = S.h0 + W.q;
+  float *seg_state = a.state + (size_t)sg.slot * a.d.H * PN;
   W.have_h = sg.init != 0;
   if (W.have_h) {
-    const float *src = a.state + hh * PN + (16 * W.ps + li) * SN + 4 * g;
+    const float *src = seg_state + hh * PN + (16 * W.ps + li) * SN + 4 * g;
 #pragma unroll
     for (int i = 0; i < 8; ++i) W.h[i] = *(const f32x4_t *)(src + 16 * i);
   } else {
@@ -625,7 +626,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void scan_ssd_pair_kernel(ScanArgs
   }
 
   if (sg.final) {
-    float *dst = (sg.final == 1 ? a.state : a.workspace) + hh * PN + (16 * W.ps + li) * SN + 4 * g;
+    float *dst = (sg.final == 1 ? seg_state : a.workspace) + hh * PN + (16 * W.ps + li) * SN + 4 * g;
 #pragma unroll
     for (int i = 0; i < 8; ++i) *(f32x4_t *)(dst + 16 * i) = W.h[i];
   }
@@ -638,8 +639,7 @@ bool ssd_pair_supported(const ScanArgs &a) {
 }
 
 hipError_t launch_scan_ssd_pair(const ScanArgs &a, const ScanMeta &m, hipStream_t s) {
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(scan_ssd_pair_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmemB);
+  hipError_t err = allow_dynamic_lds(reinterpret_cast<const void *>(scan_ssd_pair_kernel), kSmemB);
   if (err != hipSuccess) return err;
   dim3 grid(a.n_seg * (a.d.H / 2)), block(kPairThreads);
   hipLaunchKernelGGL(scan_ssd_pair_kernel, grid, block, kSmemB, s, a, m);

@@ -103,6 +103,8 @@ _SIGS = {
     "ssm_state_init": [_H, _I32, _V, _V, _V],
     "ssm_scan_workspace_bytes": [ctypes.POINTER(LayerDesc), _I64],
     "ssm_scan_chunk": [_H, _I32, _U64, _I64, _V, _V, _V, _V, _V, _V, _I32, _V, _V, _V, _SZ, _V],
+    "ssm_scan_packed": [_H, _I32, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                        ctypes.POINTER(Receipt), _V],
     "ssm_decode_step": [_H, _I32, _V, _V, _V, _V, _V, _V, _V, _V],
     "ssm_replay_log_bytes": [ctypes.POINTER(LayerDesc), _I32, _I32],
     "ssm_replay_attach": [_H, _I32, _V, _SZ],
@@ -313,6 +315,38 @@ class StreamState:
             _dev_ptr(ckpt_out, torch.float32, (n_ck, H, P, N), "ckpt_out") if n_ck else None,
             _dev_ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
         return (y, ckpt_out) if n_ck else y
+
+    def scan_packed(self, cu_seqlens, seq_slots, x, dt, B, C, y=None, final=None,
+                    receipts=False, cont=None, chunk_seq=None, stream=None):
+        """Scan packed sequences into their own slots.  cu_seqlens int[nseq+1];
+        seq_slots int[nseq]; cont u8[nseq] (continue the slot's stream) with
+        chunk_seq u64[nseq].  final: None, True (allocate [nseq,H,P,N]) or a
+        tensor.  Returns (y, final, receipts) with receipts a list of dicts
+        when requested."""
+        torch = _torch()
+        cu, cup = _host(cu_seqlens, np.int32)
+        sl, slp = _host(seq_slots, np.int32)
+        nseq = len(sl)
+        if cu.shape != (nseq + 1,):
+            raise ValueError("cu_seqlens must have nseq + 1 entries")
+        L = int(cu[-1]) if nseq else 0
+        H, P, N, G = self.H, self.P, self.N, self.G
+        if y is None:
+            y = torch.empty((L, H, P), dtype=self.io_dtype, device=x.device)
+        if final is True:
+            final = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device)
+        ct, ctp = _host(cont, np.uint8)
+        cs, csp = _host(chunk_seq, np.uint64)
+        recs = (Receipt * max(nseq, 1))() if receipts else None
+        dt_ = self.io_dtype
+        _check(_lib.ssm_scan_packed(
+            self.handle, nseq, cup, slp, ctp, csp,
+            _dev_ptr(x, dt_, (L, H, P), "x"), _dev_ptr(dt, dt_, (L, H), "dt"),
+            _dev_ptr(B, dt_, (L, G, N), "B"), _dev_ptr(C, dt_, (L, G, N), "C"),
+            _dev_ptr(y, dt_, (L, H, P), "y"),
+            None if final is None else _dev_ptr(final, torch.float32, (nseq, H, P, N), "final"),
+            recs, _stream(stream)))
+        return y, final, ([recs[i].as_dict() for i in range(nseq)] if receipts else None)
 
     # ---------------------------------------------------------------- decode
     def decode_step(self, slot_ids, x, dt, B, C, reset=None, y=None, stream=None):

@@ -38,20 +38,41 @@ def host(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
+# Margins of every comparison in this process: (test, what, margin, normwise
+# relative error, elements).  The margin is max |gpu - ref| / (atol + rtol |ref|)
+# over the tensor: 1.0 is the tolerance itself.
+MARGINS = []
+
+
+def _current_test():
+    import os
+    return os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+
+
 def assert_close(gpu, ref, rtol, atol, what=""):
+    """Elementwise |gpu - ref| <= atol + rtol |ref|; returns the margin (the
+    worst ratio of error to bound) and records it with the normwise relative
+    error ||gpu - ref|| / ||ref||."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
     assert np.isfinite(gpu).all(), f"{what}: non-finite GPU values"
     err = np.abs(gpu - ref)
     bound = atol + rtol * np.abs(ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0),
+                         np.where(err > 0, np.inf, 0.0))
+    margin = float(ratio.max()) if ratio.size else 0.0
+    rn = float(np.linalg.norm(ref.ravel()))
+    nrel = float(np.linalg.norm((gpu - ref).ravel()) / rn) if rn > 0 else float(err.max(initial=0))
+    MARGINS.append((_current_test(), what, margin, nrel, int(err.size)))
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(
             f"{what}: {int(bad.sum())}/{bad.size} elements outside tolerance "
             f"(rtol={rtol}, atol={atol}); worst at {i}: gpu={gpu[i]!r} ref={ref[i]!r}")
-    return float(err.max()) if err.size else 0.0
+    return margin
 
 
 def receipt_checksum(words):

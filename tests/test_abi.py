@@ -269,3 +269,54 @@ def test_conv_and_gate_argument_checks():
     assert gate(ssm.SSM_F32, 4, 8, 3, FAKE, FAKE, FAKE, 1e-6, FAKE, None) == ssm.SSM_E_INVALID_ARG
     assert gate(ssm.SSM_F32, 4, 8, 4, FAKE, FAKE, FAKE, -1.0, FAKE, None) == ssm.SSM_E_INVALID_ARG
     assert gate(ssm.SSM_F32, 0, 8, 8, None, None, None, 0.0, None, None) == ssm.SSM_OK
+
+
+def _packed(h, cu, slots, cont=None, seqs=None, receipts=None):
+    lib = ssm.lib()
+    n = len(slots)
+    cu_ = (ctypes.c_int32 * len(cu))(*cu)
+    sl_ = (ctypes.c_int32 * max(n, 1))(*slots)
+    ct_ = None if cont is None else (ctypes.c_uint8 * n)(*cont)
+    sq_ = None if seqs is None else (ctypes.c_uint64 * n)(*seqs)
+    return lib.ssm_scan_packed(h, n, cu_, sl_, ct_, sq_, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               receipts, None)
+
+
+def test_scan_packed_rejects_on_the_host():
+    """Packed sequences into their own slots: malformed cu_seqlens, repeated or
+    out-of-range slots, a continuing sequence whose chunk number is stale or
+    ahead, and a continuation without chunk numbers are refused with every
+    slot unchanged."""
+    lib = ssm.lib()
+    rc, h = _create(S=4)
+    pos, seq = ctypes.c_int64(-1), ctypes.c_uint64(9)
+
+    def meta(slot):
+        lib.ssm_get_position(h, slot, ctypes.byref(pos), ctypes.byref(seq))
+        return pos.value, seq.value
+
+    assert lib.ssm_scan_packed(h, -1, None, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None, None, None) == ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_scan_packed(h, 0, None, None, None, None, None, None, None, None, None,
+                               None, None, None) == ssm.SSM_OK  # nothing to do
+    assert _packed(h, [1, 4, 9], [0, 1]) == ssm.SSM_E_INVALID_ARG  # cu[0] != 0
+    assert _packed(h, [0, 5, 3], [0, 1]) == ssm.SSM_E_INVALID_ARG  # decreasing
+    assert "decreases" in _err()
+    assert _packed(h, [0, 3, 6], [2, 2]) == ssm.SSM_E_INVALID_ARG  # repeated slot
+    assert "repeated" in _err()
+    assert _packed(h, [0, 3, 6], [0, 4]) == ssm.SSM_E_INVALID_ARG  # out of range
+    assert _packed(h, [0, 3, 6], [0, 1], cont=[0, 1]) == ssm.SSM_E_INVALID_ARG  # no chunk seqs
+    assert _packed(h, [0, 3, 6], [0, 1], cont=[0, 1], seqs=[0, 1]) == ssm.SSM_E_SEQUENCE
+    assert "reordered" in _err()
+    # empty sequences only: admitted on the host with no device work (a fresh
+    # empty sequence zeroes its slot on the device, so use continuations)
+    assert _packed(h, [0, 0, 0], [0, 1], cont=[1, 1], seqs=[0, 0]) == ssm.SSM_OK
+    assert meta(0) == (0, 1) and meta(1) == (0, 1)
+    assert _packed(h, [0, 0], [1], cont=[1], seqs=[0]) == ssm.SSM_E_SEQUENCE  # duplicate
+    assert "duplicate" in _err()
+    c = ssm.Counters()
+    lib.ssm_get_counters(h, ctypes.byref(c))
+    assert c.chunks_admitted == 2 and c.chunks_rejected == 2
+    for s_ in range(4):
+        assert meta(s_)[0] == 0
+    lib.ssm_destroy(h)

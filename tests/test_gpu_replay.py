@@ -31,10 +31,16 @@ def ssm():
     (5, 5, 2, 16, 32, 1, "f32", False),    # every step flushes a full window
     (64, 16, 2, 64, 128, 1, "f32", False),  # the largest window and in-flight count (>64 KiB LDS)
     (8, 5, 2, 64, 128, 1, "f32", True),    # some dt negative (accepted input)
+    # rows that are not whole 16-byte chunks: the element-copy staging, whose
+    # x rows sit at a stride rounded up to 8 (fp32 P=6, bf16 P=12)
+    (8, 5, 2, 6, 16, 1, "f32", False),
+    (8, 5, 3, 12, 32, 1, "bf16", False),
+    (16, 5, 2, 70, 128, 1, "f32", False),  # a 6-row second tile
+    (16, 5, 2, 64, 128, 1, "f32", "xoff"),  # x 4 bytes past a 16-byte boundary
 ])
 def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, neg):
     S, b, steps = 6, 4, 40
-    say("replay small", W, n_in, H, P, N, G, io)
+    say("replay small", W, n_in, H, P, N, G, io, neg)
     A, D = inputs.params(40, H)
     st0 = np.random.default_rng(W).standard_normal((S, H, P, N)).astype(np.float32) * 0.1
     rep = ssm.StreamState(H, P, N, S, to_dev(A), to_dev(D), G=G, io_dtype=io)
@@ -52,7 +58,7 @@ def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, neg):
     for s in range(steps):
         x, dt, B, C = inputs.spec_step_inputs(s, batch=b, n_in=n_in, H=H, P=P, N=N, G=G,
                                               workload=40)
-        if neg:
+        if neg is True:
             dt = dt.copy()
             dt[:, s % n_in, s % H] = -0.02
         if io == "bf16":
@@ -61,6 +67,11 @@ def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, neg):
             dev = [bf16_dev(a) for a in bits]
         else:
             dev = [to_dev(a) for a in (x, dt, B, C)]
+        if neg == "xoff":  # the same x values behind a one-element offset
+            buf = torch.zeros(x.size + 1, dtype=torch.float32, device="cuda")
+            buf[1:] = dev[0].reshape(-1)
+            dev[0] = buf[1:].view(x.shape)
+            assert dev[0].data_ptr() % 16 != 0
         y_rep = rep.replay_step(slots, *dev)
         y_cop = cop.copy_step(slots, *dev)
         ref_y = oracle.spec_step(ref_state, ref_pos, slots, x, dt, B, C, A, D, acc[s])
@@ -88,38 +99,51 @@ def test_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, neg):
 
 @pytest.mark.parametrize("W", [8, 16, 32])
 def test_replay_workload3_full_batch(ssm, W):
-    """B=256, H=128, P=64, N=128, T=4 drafts accepted with p=0.7; the oracle
-    follows 6 sampled slots over 24 steps."""
+    """B=256, H=128, P=64, N=128, T=4 drafts accepted with p=0.7, 128 steps:
+    ReplaySSM and the copy-state-per-draft baseline on the same seeded inputs,
+    every output of every slot and step against the threaded oracle, the
+    flush count against the oracle's schedule, positions and final states."""
     Wc = inputs.W3
     B_, H, P, N, G = Wc["batch"], Wc["H"], Wc["P"], Wc["N"], Wc["G"]
-    n_in, steps = Wc["T"] + 1, 24
-    say("replay workload3", W)
+    n_in, steps = Wc["T"] + 1, Wc["steps"]
+    say("replay workload3", W, steps)
     A, D = inputs.params(3, H)
     init = inputs.device_state(3, B_, H, P, N)
     h = ssm.StreamState(H, P, N, B_, to_dev(A), to_dev(D), G=G)
     h.init(np.arange(B_), init)
     h.replay_attach(W)
+    c = ssm.StreamState(H, P, N, B_, to_dev(A), to_dev(D), G=G)
+    c.init(np.arange(B_), init)
+    c.copy_attach(n_in)
     slots = np.arange(B_, dtype=np.int32)
-    acc = inputs.acceptances(Wc["steps"], B_, T=Wc["T"], p=Wc["p"])[:steps]
+    acc = inputs.acceptances(steps, B_, T=Wc["T"], p=Wc["p"])
     sched = oracle.replay_schedule(acc, W, n_in)
-    sample = np.array([0, 3, 99, 128, 200, 255])
-    idx = torch.as_tensor(sample).long().cuda()
-    ref_state = host(init[idx])
-    ref_pos = np.zeros(len(sample), np.int64)
+    ref_state = host(init)
+    del init
+    ref_pos = np.zeros(B_, np.int64)
     for s in range(steps):
         x, dt, B, C = inputs.device_tokens(3, B_ * n_in, H, P, N, G, seed_extra=s)
         x, dt = x.view(B_, n_in, H, P), dt.view(B_, n_in, H)
         B, C = B.view(B_, n_in, G, N), C.view(B_, n_in, G, N)
         y = h.replay_step(slots, x, dt, B, C)
-        ref_y = oracle.spec_step(ref_state, ref_pos, np.arange(len(sample)), host(x[idx]),
-                                 host(dt[idx]), host(B[idx]), host(C[idx]), A, D,
-                                 acc[s][sample], n_threads=None)
-        assert_close(host(y[idx]), ref_y, what=f"y step {s}", **F32_TOL)
+        yc = c.copy_step(slots, x, dt, B, C)
+        ref_y = oracle.spec_step(ref_state, ref_pos, slots, host(x), host(dt), host(B),
+                                 host(C), A, D, acc[s], n_threads=None)
+        assert_close(host(y), ref_y, what=f"replay y step {s}", **F32_TOL)
+        assert_close(host(yc), ref_y, what=f"copy y step {s}", **F32_TOL)
         h.replay_commit(slots, acc[s])
+        c.copy_commit(slots, acc[s])
+        for b in range(B_):
+            assert h.log_state(b)[0] == sched["len_before"][s, b] + acc[s, b]
     assert h.counters()["replay_flushes"] == int(sched["flushes"].sum())
     h.materialize(slots)
-    assert_close(host(h.state[idx]), ref_state, what="state", **F32_TOL)
+    c.materialize(slots)
+    assert_close(host(h.state), ref_state, what="replay state", **F32_TOL)
+    assert_close(host(c.state), ref_state, what="copy state", **F32_TOL)
+    for b in range(B_):
+        assert h.position(b)[0] == c.position(b)[0] == ref_pos[b]
     h.destroy()
+    c.destroy()
 
 
 def test_replay_alone_matches_decode(ssm):
