@@ -238,6 +238,30 @@ ssm_status ssm_scan_packed(ssm_handle h, int32_t nseq, const int32_t *h_cu_seqle
                            const void *B, const void *C, void *y, float *d_final,
                            ssm_receipt *h_receipts, void *stream);
 
+/* Bytes of workspace ssm_scan_chunk_static has: the size of the library's
+ * static device scratch (16 MiB per GPU). */
+#define SSM_STATIC_WORKSPACE_BYTES ((size_t)16 << 20)
+
+/* ssm_scan_chunk for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same chunk scan, arguments and results, with no workspace argument.  Its
+ * workspace is the library's static device scratch, SSM_STATIC_WORKSPACE_BYTES
+ * per GPU, which each GPU holds from the library's load until the process
+ * ends; the call allocates and frees nothing (with SSM_FLAG_CHECK_FINITE the
+ * finite-check flag lives there too).  The form is chosen as ssm_scan_chunk
+ * chooses it for a workspace of that size: the tile-parallel form when
+ * ssm_scan_workspace_bytes(desc, L) fits, else the recurrent or SSD form.  A
+ * chunk that carries state in and resets later needs H*P*N*4 bytes of it; a
+ * layer whose state is larger is refused with SSM_E_INVALID_ARG (nothing
+ * changed).  Every call on one GPU shares that GPU's scratch, and the scratch
+ * keeps what the last call left in it: calls that overlap on one GPU (on
+ * different streams, or from several host threads) race and must not be
+ * issued; calls in order on one stream are safe. */
+ssm_status ssm_scan_chunk_static(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_t L,
+                                 const void *x, const void *dt, const void *B, const void *C,
+                                 const uint8_t *h_reset, void *y, int32_t n_ckpt,
+                                 const int64_t *h_ckpt_at, float *d_ckpt_out, void *stream);
+
 /* ------------------------------------------------------------------ decode */
 
 /* One token for each of `batch` distinct slots h_slot_ids[batch] (decode moves

@@ -206,12 +206,18 @@ void release_scratch(Handle *H) {
   H->scratch = nullptr;
 }
 
-// Device-side finite check of a list of io-dtype buffers; synchronises.
-ssm_status check_finite(Handle *H, hipStream_t s, std::initializer_list<std::pair<const void *, size_t>> bufs) {
+// Device-side finite check of a list of io-dtype buffers; synchronises.  The
+// flag (8 bytes of device memory) is the handle's scratch, or `fixed_flag`.
+ssm_status check_finite(Handle *H, hipStream_t s,
+                        std::initializer_list<std::pair<const void *, size_t>> bufs,
+                        unsigned int *fixed_flag = nullptr) {
   if (!(H->flags & SSM_FLAG_CHECK_FINITE)) return SSM_OK;
-  ssm_status st = ensure_scratch(H);
-  if (st != SSM_OK) return st;
-  unsigned int *flag = reinterpret_cast<unsigned int *>((char *)H->scratch + kFlagOff);
+  unsigned int *flag = fixed_flag;
+  if (!flag) {
+    ssm_status st = ensure_scratch(H);
+    if (st != SSM_OK) return st;
+    flag = reinterpret_cast<unsigned int *>((char *)H->scratch + kFlagOff);
+  }
   HIP_TRY(launch_zero_u64(reinterpret_cast<unsigned long long *>(flag), 1, s));
   for (auto &b : bufs) HIP_TRY(launch_finite_check(H->io, b.first, b.second, flag, s));
   unsigned int host = 0;
@@ -494,12 +500,15 @@ size_t ssm_scan_workspace_bytes(const ssm_layer_desc *desc, int64_t L) {
   return std::max(state, chunk_ws_floats(d, L) * sizeof(float));
 }
 
-ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_t L,
-                          const void *x, const void *dt, const void *B, const void *C,
-                          const uint8_t *h_reset, void *y, int32_t n_ckpt,
-                          const int64_t *h_ckpt_at, float *d_ckpt_out, void *d_workspace,
-                          size_t ws_bytes, void *stream) {
-  GET_HANDLE(H, h);
+// The chunk scan behind ssm_scan_chunk and ssm_scan_chunk_static.  With
+// `fixed_flag` set, the workspace is the library's static scratch (its size is
+// not the caller's to change) and the finite-check flag lives there too.
+static ssm_status scan_chunk_impl(Handle *H, int32_t slot, uint64_t chunk_seq, int64_t L,
+                                  const void *x, const void *dt, const void *B, const void *C,
+                                  const uint8_t *h_reset, void *y, int32_t n_ckpt,
+                                  const int64_t *h_ckpt_at, float *d_ckpt_out, void *d_workspace,
+                                  size_t ws_bytes, unsigned int *fixed_flag, void *stream) {
+  const bool fixed = fixed_flag != nullptr;
   if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "scan: slot %d out of range", slot);
   Slot &sl = H->slots[slot];
   if (chunk_seq != sl.chunk_seq) {
@@ -544,7 +553,7 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
                    ws_bytes >= chunk_ws_floats(H->d, L) * sizeof(float);
   if (par) {
     st = check_finite(H, s, {{x, (size_t)L * H->d.H * H->d.P}, {dt, (size_t)L * H->d.H},
-                             {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
+                             {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}}, fixed_flag);
     if (st != SSM_OK) return st;
     const int64_t piece = (int64_t)kChunkTile * kChunkTilesPerLaunch;
     for (int64_t t0 = 0; t0 < L; t0 += piece) {
@@ -592,14 +601,22 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
   }
   const bool need_ws = !par && segs.size() > 1 && segs.front().init;
   segs.back().final = need_ws ? 2 : 1;
-  if (need_ws && (!d_workspace || ws_bytes < H->state_bytes()))
+  if (need_ws && (!d_workspace || ws_bytes < H->state_bytes())) {
+    if (fixed)
+      return fail(SSM_E_INVALID_ARG,
+                  "scan (static scratch): this chunk carries state in and resets later; it "
+                  "needs %zu bytes of workspace, above the static scratch's %zu (use "
+                  "ssm_scan_chunk with a workspace, or split the chunk at the reset)",
+                  H->state_bytes(), ws_bytes);
     return fail(SSM_E_INVALID_ARG,
                 "scan: this chunk carries state in and resets later; it needs a workspace of "
                 "%zu bytes",
                 H->state_bytes());
+  }
   if (!par) {
     st = check_finite(H, s, {{x, (size_t)L * H->d.H * H->d.P}, {dt, (size_t)L * H->d.H},
-                             {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}});
+                             {B, (size_t)L * H->d.G * H->d.N}, {C, (size_t)L * H->d.G * H->d.N}},
+                      fixed_flag);
     if (st != SSM_OK) return st;
   }
   if (!par) {
@@ -623,6 +640,28 @@ ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_
   if (segs.front().init) H->cnt.state_bytes_read += H->state_bytes();
   H->cnt.state_bytes_written += H->state_bytes() * (1 + (size_t)n_ckpt);
   return SSM_OK;
+}
+
+ssm_status ssm_scan_chunk(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_t L,
+                          const void *x, const void *dt, const void *B, const void *C,
+                          const uint8_t *h_reset, void *y, int32_t n_ckpt,
+                          const int64_t *h_ckpt_at, float *d_ckpt_out, void *d_workspace,
+                          size_t ws_bytes, void *stream) {
+  GET_HANDLE(H, h);
+  return scan_chunk_impl(H, slot, chunk_seq, L, x, dt, B, C, h_reset, y, n_ckpt, h_ckpt_at,
+                         d_ckpt_out, d_workspace, ws_bytes, nullptr, stream);
+}
+
+ssm_status ssm_scan_chunk_static(ssm_handle h, int32_t slot, uint64_t chunk_seq, int64_t L,
+                                 const void *x, const void *dt, const void *B, const void *C,
+                                 const uint8_t *h_reset, void *y, int32_t n_ckpt,
+                                 const int64_t *h_ckpt_at, float *d_ckpt_out, void *stream) {
+  GET_HANDLE(H, h);
+  char *base = nullptr;  // this device's copy of the static scratch
+  HIP_TRY(static_scratch((void **)&base));
+  return scan_chunk_impl(H, slot, chunk_seq, L, x, dt, B, C, h_reset, y, n_ckpt, h_ckpt_at,
+                         d_ckpt_out, base, SSM_STATIC_WORKSPACE_BYTES,
+                         reinterpret_cast<unsigned int *>(base + kStaticFlagOff), stream);
 }
 
 ssm_status ssm_scan_packed(ssm_handle h, int32_t nseq, const int32_t *h_cu_seqlens,

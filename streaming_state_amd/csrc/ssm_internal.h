@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ssm_stream.h"
+
 namespace ssm {
 
 // Batch entries per launch for decode / copy / replay.  Per-entry metadata
@@ -169,6 +171,14 @@ struct ChunkArgs {
 bool chunk_supported(int io, const Dims &d);
 size_t chunk_ws_floats(const Dims &d, int64_t L);
 hipError_t launch_chunk(int io, const ChunkArgs &a, const ChunkMeta &m, hipStream_t s);
+
+// ------------------------------------------------------ static device scratch
+// A file-scope device array (ssm_static.hip): the workspace of
+// ssm_scan_chunk_static, then the finite-check flag.
+constexpr size_t kStaticFlagOff = SSM_STATIC_WORKSPACE_BYTES;
+constexpr size_t kStaticScratchBytes = kStaticFlagOff + 256;
+// This device's copy of the array (its address looked up once per device).
+hipError_t static_scratch(void **out);
 
 // --------------------------------------------------------------- state ops
 hipError_t launch_zero(float *dst, size_t n_floats, hipStream_t s);

@@ -52,6 +52,7 @@ SSM_E_LOG = -6
 SSM_E_HIP = -7
 SSM_F32, SSM_F16, SSM_BF16 = 0, 1, 2
 SSM_FLAG_CHECK_FINITE = 1
+SSM_STATIC_WORKSPACE_BYTES = 16 << 20
 
 _NAMES = {0: "SSM_OK", -1: "SSM_E_INVALID_ARG", -2: "SSM_E_INVALID_CHUNK",
           -3: "SSM_E_INVALID_STATE", -4: "SSM_E_SEQUENCE", -5: "SSM_E_SCHEMA", -6: "SSM_E_LOG",
@@ -103,6 +104,7 @@ _SIGS = {
     "ssm_state_init": [_H, _I32, _V, _V, _V],
     "ssm_scan_workspace_bytes": [ctypes.POINTER(LayerDesc), _I64],
     "ssm_scan_chunk": [_H, _I32, _U64, _I64, _V, _V, _V, _V, _V, _V, _I32, _V, _V, _V, _SZ, _V],
+    "ssm_scan_chunk_static": [_H, _I32, _U64, _I64, _V, _V, _V, _V, _V, _V, _I32, _V, _V, _V],
     "ssm_scan_packed": [_H, _I32, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                         ctypes.POINTER(Receipt), _V],
     "ssm_decode_step": [_H, _I32, _V, _V, _V, _V, _V, _V, _V, _V],
@@ -314,6 +316,32 @@ class StreamState:
             _dev_ptr(y, dt_, (L, H, P), "y"), n_ck, ckp if n_ck else None,
             _dev_ptr(ckpt_out, torch.float32, (n_ck, H, P, N), "ckpt_out") if n_ck else None,
             _dev_ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+        return (y, ckpt_out) if n_ck else y
+
+    def scan_chunk_static(self, slot, chunk_seq, x, dt, B, C, y=None, reset=None, ckpt_at=None,
+                          ckpt_out=None, stream=None):
+        """scan_chunk with the library's static device scratch as workspace
+        (no device memory is allocated by the call)."""
+        torch = _torch()
+        L = x.shape[0]
+        H, P, N, G = self.H, self.P, self.N, self.G
+        if y is None:
+            y = torch.empty((L, H, P), dtype=self.io_dtype, device=x.device)
+        rs, rp = _host(reset, np.uint8)
+        if rs is not None and rs.shape != (L,):
+            raise ValueError("reset must be u8[L]")
+        ck, ckp = _host(ckpt_at if ckpt_at is not None else [], np.int64)
+        n_ck = len(ck)
+        if n_ck and ckpt_out is None:
+            ckpt_out = torch.empty((n_ck, H, P, N), dtype=torch.float32, device=x.device)
+        dt_ = self.io_dtype
+        _check(_lib.ssm_scan_chunk_static(
+            self.handle, int(slot), int(chunk_seq), int(L),
+            _dev_ptr(x, dt_, (L, H, P), "x"), _dev_ptr(dt, dt_, (L, H), "dt"),
+            _dev_ptr(B, dt_, (L, G, N), "B"), _dev_ptr(C, dt_, (L, G, N), "C"), rp,
+            _dev_ptr(y, dt_, (L, H, P), "y"), n_ck, ckp if n_ck else None,
+            _dev_ptr(ckpt_out, torch.float32, (n_ck, H, P, N), "ckpt_out") if n_ck else None,
+            _stream(stream)))
         return (y, ckpt_out) if n_ck else y
 
     def scan_packed(self, cu_seqlens, seq_slots, x, dt, B, C, y=None, final=None,
