@@ -11,7 +11,8 @@ module only marshals numpy arrays into it.  ``acceptance.py`` and
 of the replay flush schedule; ``blob.py`` reads and writes the state-blob byte
 format of the recurrent-state companion store; ``conv.py`` holds the causal
 depthwise conv1d with its carried conv state and the gated output (numpy,
-fp64).
+fp64).  ``gdn_oracle.c`` (marshalled by ``gdn.py``) holds the Gated DeltaNet
+recurrence and its replay form.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against the pages and
 the mathematics (worked example, closed forms, brute force); none is "parity
@@ -23,3 +24,10 @@ from .core import (  # noqa: F401
 )
 from .acceptance import tokens_kept, copy_rule, expected_kept  # noqa: F401
 from .schedule import replay_schedule  # noqa: F401
+from . import gdn  # noqa: F401
+
+
+def build_all():
+    """Compile every C part of the oracle."""
+    build()
+    gdn.build()

@@ -31,7 +31,7 @@ import numpy as np
 
 BASE_SEED = 20261202
 _TENSOR_IDS = {"x": 1, "dt": 2, "B": 3, "C": 4, "A": 5, "D": 6, "state": 7, "reset": 8,
-               "accept": 9, "lengths": 10, "slots": 11}
+               "accept": 9, "lengths": 10, "slots": 11, "beta": 12, "k": 13, "q": 14}
 
 
 def rng(workload, tensor, *extra):
@@ -268,3 +268,45 @@ def device_state(workload, S, H, P, N, std=0.02, device="cuda"):
 def device_resets(workload, step, batch, p=0.02):
     """Per-slot reset flags of one decode step (host u8[batch])."""
     return (rng(workload, "reset", step).random(batch) < p).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet verify workload (the pages name the recurrence but give no
+# workload): B=256 slots of one layer with 32 value heads over 16 key groups,
+# head dims 128 x 128 (2 MiB of fp32 state per slot), T = 4 drafts, p = 0.7,
+# windows 8, 16, 32.
+# ---------------------------------------------------------------------------
+W5 = dict(batch=256, H=32, G=16, P=128, N=128, steps=128, T=4, p=0.7, windows=(8, 16, 32))
+
+
+def gdn_tokens(workload, L, H, P, N, G=1, *extra):
+    """v[L,H,P] ~ N(0,1); k[L,G,N] unit-norm (a N(0,I) draw divided by its
+    norm) and q[L,G,N] unit-norm times N^-1/2 (how such layers feed keys and
+    queries); beta[L,H] = sigmoid(N(0,1)); dt[L,H] = softplus(N(-2, 0.5)), the
+    gate's step as for Mamba-2.  fp32."""
+    v = rng(workload, "x", *extra).standard_normal((L, H, P), dtype=np.float32)
+    z = rng(workload, "dt", *extra).normal(-2.0, 0.5, size=(L, H))
+    dt = _softplus(z).astype(np.float32)
+    bz = rng(workload, "beta", *extra).standard_normal((L, H))
+    beta = (1.0 / (1.0 + np.exp(-bz))).astype(np.float32)
+    k = rng(workload, "k", *extra).standard_normal((L, G, N))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    q = rng(workload, "q", *extra).standard_normal((L, G, N))
+    q = (q / np.linalg.norm(q, axis=-1, keepdims=True) / np.sqrt(N)).astype(np.float32)
+    return v, dt, beta, k, q
+
+
+def device_gdn_tokens(workload, L, H, P, N, G=1, seed_extra=0, device="cuda"):
+    """The same distributions drawn on the device with a seeded torch
+    generator (fp32): v, dt, beta, k, q."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((BASE_SEED + workload) * 1000003 + int(seed_extra))
+    v = torch.randn((L, H, P), generator=g, device=device)
+    dt = torch.nn.functional.softplus(torch.randn((L, H), generator=g, device=device) * 0.5 - 2.0)
+    beta = torch.sigmoid(torch.randn((L, H), generator=g, device=device))
+    k = torch.randn((L, G, N), generator=g, device=device)
+    k = k / k.norm(dim=-1, keepdim=True)
+    q = torch.randn((L, G, N), generator=g, device=device)
+    q = q / q.norm(dim=-1, keepdim=True) / float(np.sqrt(N))
+    return v, dt, beta, k, q

@@ -14,10 +14,12 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session", autouse=True)
 def _oracle_built():
-    # The oracle is a plain C file; build it once if this tree has no copy yet.
+    # The oracle is plain C; build it once if this tree has no copy yet.
     import oracle
     if not os.path.exists(oracle.lib_path()):
         oracle.build()
+    if not os.path.exists(oracle.gdn.lib_path()):
+        oracle.gdn.build()
     yield
 
 
