@@ -80,13 +80,35 @@ typedef enum { SSM_F32 = 0, SSM_F16 = 1, SSM_BF16 = 2 } ssm_dtype;
                                     with nothing changed (the runnable
                                     artifact's "invalid_chunk") */
 
+/* The recurrence a handle's state follows.
+ *   SSM_MAMBA2       the selective-scan recurrence above.
+ *   SSM_GATED_DELTA  the gated delta rule of Gated DeltaNet, per value head h
+ *                    with key group g:
+ *                      S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *                      o_t = S_t q_t,   alpha_t = exp(dt_t[h] * A[h])
+ *                    with S [P value rows, N key columns] in the same
+ *                    state[S,H,P,N] layout; x carries v [.,H,P], B carries
+ *                    k and C carries q [.,G,N], beta [.,H] is an extra
+ *                    input, D is unused.  The pages name it among the
+ *                    recurrences whose update unrolls into a decay plus a
+ *                    sum, so that replay applies ("Why Speculative Decoding
+ *                    Slows Hybrid Mamba Models at Large Batch Sizes", section
+ *                    "When Replaying the Inputs Is the Wrong Tool"); the
+ *                    update itself is the published gated delta rule.  Its
+ *                    handles serve the verify paths (ssm_gdn_replay_step,
+ *                    ssm_gdn_copy_step) and the state operations. */
+typedef enum { SSM_MAMBA2 = 0, SSM_GATED_DELTA = 1 } ssm_recurrence;
+
 /* Layer description.  Supported: H,P >= 1; N % 4 == 0 and 4 <= N <= 128;
- * G >= 1 with H % G == 0; io_dtype SSM_F32 or SSM_BF16. */
+ * G >= 1 with H % G == 0; io_dtype SSM_F32 or SSM_BF16; recurrence an
+ * ssm_recurrence (0, the default of a zeroed struct, is Mamba-2). */
 typedef struct {
   int32_t H, P, N, G;
   int32_t io_dtype;        /* ssm_dtype of x, dt, B, C and y */
   uint32_t schema_version; /* caller's state-schema version */
   uint64_t model_rev;      /* caller's model revision */
+  int32_t recurrence;      /* ssm_recurrence */
+  int32_t reserved;        /* 0 */
 } ssm_layer_desc;
 
 /* Checkpoint receipt: the fields a resume must match ("Mamba Streaming State
@@ -104,6 +126,10 @@ typedef struct {
   uint64_t chunk_seq;      /* next chunk sequence number the stream expects */
   uint64_t checksum;       /* sum over the state's 32-bit words w_i of
                               w_i * (2*i + 1), modulo 2^64, i in [H,P,N] order */
+  uint32_t recurrence;     /* ssm_recurrence of the state (states of different
+                              recurrences never resume into each other:
+                              section "Version state semantics for Mamba-3") */
+  uint32_t reserved;
 } ssm_receipt;
 
 /* Lifecycle counters (resets, rejected duplicate or reordered chunks,
@@ -135,8 +161,8 @@ typedef int64_t ssm_handle;
  * fixed-size fp32 array per stream and layer ("Why Speculative Decoding Slows
  * Hybrid Mamba Models at Large Batch Sizes", section "The Problem").
  * flags: SSM_FLAG_*.  No device call is made.  Errors: SSM_E_INVALID_ARG for
- * a bad desc, n_slots < 1, a NULL or misaligned (16 bytes) state, NULL A/D,
- * or unknown flags. */
+ * a bad desc, n_slots < 1, a NULL or misaligned (16 bytes) state, NULL A (or
+ * NULL D for Mamba-2; Gated DeltaNet takes D = NULL), or unknown flags. */
 ssm_status ssm_create(const ssm_layer_desc *desc, int32_t n_slots, float *d_state,
                       const float *d_A, const float *d_D, uint32_t flags, ssm_handle *out);
 
@@ -277,8 +303,9 @@ ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
 
 /* ------------------------------------------------------------------ replay */
 
-/* Bytes of the replay log for n_slots slots and window W: per slot W entries of
- * dt[H], x[H,P] and B[G,N] in the io dtype. */
+/* Bytes of the replay log for n_slots slots and window W: per slot two halves
+ * of W entries of dt[H], x[H,P] and B[G,N] (Gated DeltaNet: also beta[H]) in
+ * the io dtype, plus scratch. */
 size_t ssm_replay_log_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t W);
 
 /* Attach the caller's log buffer (device, ssm_replay_log_bytes bytes) with
@@ -299,6 +326,18 @@ ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_by
 ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
                            const void *x, const void *dt, const void *B, const void *C, void *y,
                            void *stream);
+
+/* ReplaySSM verify of a Gated DeltaNet handle (desc.recurrence =
+ * SSM_GATED_DELTA): as ssm_replay_step, with v[batch,n_in,H,P],
+ * dt[batch,n_in,H], beta[batch,n_in,H], k,q[batch,n_in,G,N] and
+ * o[batch,n_in,H,P].  Outputs come from the checkpoint and the log: each
+ * in-flight query is carried back through the logged entries' rank-1 factors
+ * alpha_j (I - beta_j k_j k_j^T) and meets the checkpoint once; the state is
+ * written only when the log is full and is folded in.  Commit with
+ * ssm_replay_commit; ssm_state_materialize folds a log into the state. */
+ssm_status ssm_gdn_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                               int32_t n_in, const void *v, const void *dt, const void *beta,
+                               const void *k, const void *q, void *o, void *stream);
 
 /* Commit the last replay step of each slot: h_accepted[i] (1..n_in) leading
  * in-flight tokens join the log and the position; the rest are dropped (they
@@ -325,6 +364,12 @@ ssm_status ssm_copy_attach(ssm_handle h, int32_t n_in_max, float *d_copies, size
 ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
                          const void *x, const void *dt, const void *B, const void *C, void *y,
                          void *stream);
+
+/* The copy-state-per-draft verify of a Gated DeltaNet handle (the baseline
+ * of ssm_gdn_replay_step; same layouts), committed with ssm_copy_commit. */
+ssm_status ssm_gdn_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                             const void *v, const void *dt, const void *beta, const void *k,
+                             const void *q, void *o, void *stream);
 
 /* Adopt copy h_accepted[i]-1 as the slot's live state (an index move, no data
  * copied) and advance the position.  Host only. */

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm_stream.so")
 LATENCY = os.path.join(HERE, "ssm_abi_latency")
-SOURCES = ["ssm_host.cpp", "ssm_decode.hip", "ssm_kernels.hip", "ssm_scan.hip", "ssm_ssd.hip", "ssm_ssd_pair.hip", "ssm_chunk.hip", "ssm_conv.hip", "ssm_static.hip"]
+SOURCES = ["ssm_host.cpp", "ssm_decode.hip", "ssm_kernels.hip", "ssm_scan.hip", "ssm_ssd.hip", "ssm_ssd_pair.hip", "ssm_chunk.hip", "ssm_conv.hip", "ssm_static.hip", "ssm_gdn.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -275,6 +275,76 @@ __device__ __forceinline__ void nt_store4(float *p, float4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t *>(p));
 }
 
+// ------------------------------------------------------------ LDS staging
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Copy n 16-byte chunks global -> LDS: chunk i lands at lds + 16 i, read from
+// src_of(i).  Each wave instruction fills 64 consecutive chunks (lane l
+// writes 16 bytes at the wave's LDS base + 16 l; inactive lanes write
+// nothing).  The copies complete asynchronously: wait on vmcnt before use.
+template <typename SrcOf>
+__device__ __forceinline__ void stage_lds(char *lds, int n, SrcOf src_of) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  for (int blk = wave; blk * 64 < n; blk += kThreads / 64) {
+    const int i = blk * 64 + lane;
+    if (i < n)
+      __builtin_amdgcn_global_load_lds(src_of(i), (lds_void_t *)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+template <typename T> __device__ __forceinline__ float4 lds_ld4(const T *p);
+template <> __device__ __forceinline__ float4 lds_ld4<float>(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+template <> __device__ __forceinline__ float4 lds_ld4<bf16_t>(const bf16_t *p) {
+  const uint2 r = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+}
+
+// R consecutive io values from LDS (16-byte aligned) as floats.
+template <typename T, int R> __device__ __forceinline__ void lds_ld_rows(const T *p, float *v) {
+  static_assert((R * sizeof(T)) % 16 == 0, "whole 16-byte reads");
+#pragma unroll
+  for (int q = 0; q < (int)(R * sizeof(T)) / 16; ++q) {
+    const uint4 u = reinterpret_cast<const uint4 *>(p)[q];
+    if (sizeof(T) == 4) {
+      v[4 * q + 0] = __uint_as_float(u.x);
+      v[4 * q + 1] = __uint_as_float(u.y);
+      v[4 * q + 2] = __uint_as_float(u.z);
+      v[4 * q + 3] = __uint_as_float(u.w);
+    } else {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[8 * q + 2 * t] = __uint_as_float(w[t] << 16);
+        v[8 * q + 2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// Sum over the 32 lanes of a row group (lanes 0-31 or 32-63), left in every
+// one of them: rotations by 1, 2, 4 and 8 inside each 16-lane row give each
+// lane its row's sum, and v_permlane16_swap adds the other row of the pair.
+__device__ __forceinline__ float allsum32(float v) {
+  v += dpp_f<0x121>(v);  // row_ror:1
+  v += dpp_f<0x122>(v);  // row_ror:2
+  v += dpp_f<0x124>(v);  // row_ror:4
+  v += dpp_f<0x128>(v);  // row_ror:8
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The same over all 64 lanes of the wave (v_permlane32_swap adds the halves).
+__device__ __forceinline__ float allsum64(float v) {
+  v = allsum32(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ----------------------------------------------------------- wave prefix sum
 // Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 within each
 // 16-lane row, then row 15's and row 31's totals broadcast forward.

@@ -54,6 +54,7 @@ struct Handle {
   ssm_layer_desc desc;
   Dims d;
   int io;
+  int rec;  // SSM_MAMBA2 or SSM_GATED_DELTA
   int S;
   float *state;
   const float *A, *D;
@@ -136,7 +137,16 @@ ssm_status check_desc(const ssm_layer_desc *desc) {
                 desc->N);
   if (desc->io_dtype != SSM_F32 && desc->io_dtype != SSM_BF16)
     return fail(SSM_E_INVALID_ARG, "io_dtype %d not supported (fp32 or bf16)", desc->io_dtype);
+  if (desc->recurrence != SSM_MAMBA2 && desc->recurrence != SSM_GATED_DELTA)
+    return fail(SSM_E_INVALID_ARG, "unknown recurrence %d", desc->recurrence);
   return SSM_OK;
+}
+
+// Calls of one recurrence refuse handles of the other.
+ssm_status need_rec(const Handle *H, int rec, const char *what) {
+  if (H->rec == rec) return SSM_OK;
+  return fail(SSM_E_INVALID_ARG, "%s: this handle holds a %s layer", what,
+              H->rec == SSM_GATED_DELTA ? "Gated DeltaNet" : "Mamba-2");
 }
 
 Dims dims_of(const ssm_layer_desc *desc) {
@@ -295,7 +305,10 @@ ssm_status fold_logs(Handle *H, const std::vector<int> &slots, hipStream_t s) {
     a.n_in = 0;
     a.W = H->W;
     a.nin_magic = fastdiv_magic(a.n_in);
-    HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
+    if (H->rec == SSM_GATED_DELTA)
+      HIP_TRY(launch_gdn_replay(H->io, a, m, H->lay, s));
+    else
+      HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
   }
   for (int sidx : slots) {
     Slot &sl = H->slots[sidx];
@@ -349,6 +362,7 @@ ssm_receipt slot_receipt(const Handle *H, const Slot &sl, uint64_t sum) {
   r.position = sl.pos;
   r.chunk_seq = sl.chunk_seq;
   r.checksum = sum;
+  r.recurrence = (uint32_t)H->rec;
   return r;
 }
 
@@ -417,13 +431,15 @@ ssm_status ssm_create(const ssm_layer_desc *desc, int32_t n_slots, float *d_stat
   if (st != SSM_OK) return st;
   if (!out) return fail(SSM_E_INVALID_ARG, "out is NULL");
   if (n_slots < 1) return fail(SSM_E_INVALID_ARG, "n_slots must be >= 1");
-  if (!d_state || !d_A || !d_D) return fail(SSM_E_INVALID_ARG, "state, A and D are required");
+  if (!d_state || !d_A || (!d_D && desc->recurrence == SSM_MAMBA2))
+    return fail(SSM_E_INVALID_ARG, "state, A and (for Mamba-2) D are required");
   if (flags & ~SSM_FLAG_CHECK_FINITE) return fail(SSM_E_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!aligned(d_state, 16)) return fail(SSM_E_INVALID_ARG, "state must be 16-byte aligned");
   Handle *H = new Handle();
   H->desc = *desc;
   H->d = dims_of(desc);
   H->io = desc->io_dtype;
+  H->rec = desc->recurrence;
   H->S = n_slots;
   H->state = d_state;
   H->A = d_A;
@@ -509,6 +525,7 @@ static ssm_status scan_chunk_impl(Handle *H, int32_t slot, uint64_t chunk_seq, i
                                   const int64_t *h_ckpt_at, float *d_ckpt_out, void *d_workspace,
                                   size_t ws_bytes, unsigned int *fixed_flag, void *stream) {
   const bool fixed = fixed_flag != nullptr;
+  if (ssm_status st0 = need_rec(H, SSM_MAMBA2, "scan"); st0 != SSM_OK) return st0;
   if (slot < 0 || slot >= H->S) return fail(SSM_E_INVALID_ARG, "scan: slot %d out of range", slot);
   Slot &sl = H->slots[slot];
   if (chunk_seq != sl.chunk_seq) {
@@ -670,6 +687,7 @@ ssm_status ssm_scan_packed(ssm_handle h, int32_t nseq, const int32_t *h_cu_seqle
                            const void *B, const void *C, void *y, float *d_final,
                            ssm_receipt *h_receipts, void *stream) {
   GET_HANDLE(H, h);
+  if (ssm_status st0 = need_rec(H, SSM_MAMBA2, "scan packed"); st0 != SSM_OK) return st0;
   if (nseq < 0) return fail(SSM_E_INVALID_ARG, "scan packed: negative sequence count");
   if (nseq == 0) return SSM_OK;
   if (!h_cu_seqlens) return fail(SSM_E_INVALID_ARG, "scan packed: cu_seqlens is NULL");
@@ -778,6 +796,7 @@ ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
                            const void *x, const void *dt, const void *B, const void *C,
                            const uint8_t *h_reset, void *y, void *stream) {
   GET_HANDLE(H, h);
+  if (ssm_status st0 = need_rec(H, SSM_MAMBA2, "decode"); st0 != SSM_OK) return st0;
   ssm_status st = check_slots(H, batch, h_slot_ids, "decode");
   if (st != SSM_OK) return st;
   for (int i = 0; i < batch; ++i) {
@@ -833,7 +852,7 @@ ssm_status ssm_decode_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
 size_t ssm_replay_log_bytes(const ssm_layer_desc *desc, int32_t n_slots, int32_t W) {
   if (check_desc(desc) != SSM_OK || n_slots < 1 || W < 1 || W > kMaxW) return 0;
   const Dims d{desc->H, desc->P, desc->N, desc->G, (desc->P + kRows - 1) / kRows};
-  return log_layout(desc->io_dtype, d, n_slots, W).total;
+  return log_layout(desc->io_dtype, d, n_slots, W, desc->recurrence == SSM_GATED_DELTA).total;
 }
 
 ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_bytes) {
@@ -841,7 +860,7 @@ ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_by
   if (W < 1 || W > kMaxW) return fail(SSM_E_INVALID_ARG, "replay: W must be in [1, %d]", kMaxW);
   if (!d_log || !aligned(d_log, 256))
     return fail(SSM_E_INVALID_ARG, "replay: log must be non-NULL and 256-byte aligned");
-  const LogLayout lay = log_layout(H->io, H->d, H->S, W);
+  const LogLayout lay = log_layout(H->io, H->d, H->S, W, H->rec == SSM_GATED_DELTA);
   if (log_bytes < lay.total)
     return fail(SSM_E_INVALID_ARG, "replay: log needs %zu bytes, got %zu", lay.total, log_bytes);
   for (int s = 0; s < H->S; ++s)
@@ -857,10 +876,9 @@ ssm_status ssm_replay_attach(ssm_handle h, int32_t W, void *d_log, size_t log_by
   return SSM_OK;
 }
 
-ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
-                           const void *x, const void *dt, const void *B, const void *C, void *y,
-                           void *stream) {
-  GET_HANDLE(H, h);
+static ssm_status replay_step_impl(Handle *H, int32_t batch, const int32_t *h_slot_ids,
+                                   int32_t n_in, const void *x, const void *dt, const void *beta,
+                                   const void *B, const void *C, void *y, void *stream) {
   if (!H->log) return fail(SSM_E_LOG, "replay: no log attached");
   if (n_in < 1 || n_in > H->W || n_in > kMaxInFlight)
     return fail(SSM_E_INVALID_ARG, "replay: n_in must be in [1, min(W, %d)]", kMaxInFlight);
@@ -881,8 +899,11 @@ ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
   hipStream_t s = as_stream(stream);
   const Dims &d = H->d;
   const size_t nt = (size_t)batch * n_in;
+  const bool gdn = H->rec == SSM_GATED_DELTA;
+  if (gdn && (!beta || !aligned(beta, io_size(H->io))))
+    return fail(SSM_E_INVALID_ARG, "replay: beta is NULL or misaligned");
   st = check_finite(H, s, {{x, nt * d.H * d.P}, {dt, nt * d.H}, {B, nt * d.G * d.N},
-                           {C, nt * d.G * d.N}});
+                           {C, nt * d.G * d.N}, {gdn ? beta : nullptr, gdn ? nt * d.H : 0}});
   if (st != SSM_OK) return st;
   const size_t es = io_size(H->io);
   for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
@@ -900,6 +921,7 @@ ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
     ReplayArgs a{};
     a.x = (const char *)x + off * d.H * d.P * es;
     a.dt = (const char *)dt + off * d.H * es;
+    a.beta = gdn ? (const char *)beta + off * d.H * es : nullptr;
     a.B = (const char *)B + off * d.G * d.N * es;
     a.C = (const char *)C + off * d.G * d.N * es;
     a.y = (char *)y + off * d.H * d.P * es;
@@ -913,7 +935,10 @@ ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
     a.n_in = n_in;
     a.W = H->W;
     a.nin_magic = fastdiv_magic(a.n_in);
-    HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
+    if (gdn)
+      HIP_TRY(launch_gdn_replay(H->io, a, m, H->lay, s));
+    else
+      HIP_TRY(launch_replay(H->io, a, m, H->lay, s));
   }
   for (int i = 0; i < batch; ++i) {
     Slot &sl = H->slots[h_slot_ids[i]];
@@ -930,6 +955,22 @@ ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_id
   }
   H->cnt.replay_steps++;
   return SSM_OK;
+}
+
+ssm_status ssm_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                           const void *x, const void *dt, const void *B, const void *C, void *y,
+                           void *stream) {
+  GET_HANDLE(H, h);
+  if (ssm_status st = need_rec(H, SSM_MAMBA2, "replay"); st != SSM_OK) return st;
+  return replay_step_impl(H, batch, h_slot_ids, n_in, x, dt, nullptr, B, C, y, stream);
+}
+
+ssm_status ssm_gdn_replay_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
+                               int32_t n_in, const void *v, const void *dt, const void *beta,
+                               const void *k, const void *q, void *y, void *stream) {
+  GET_HANDLE(H, h);
+  if (ssm_status st = need_rec(H, SSM_GATED_DELTA, "gdn replay"); st != SSM_OK) return st;
+  return replay_step_impl(H, batch, h_slot_ids, n_in, v, dt, beta, k, q, y, stream);
 }
 
 ssm_status ssm_replay_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
@@ -979,10 +1020,9 @@ ssm_status ssm_copy_attach(ssm_handle h, int32_t n_in_max, float *d_copies, size
   return SSM_OK;
 }
 
-ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
-                         const void *x, const void *dt, const void *B, const void *C, void *y,
-                         void *stream) {
-  GET_HANDLE(H, h);
+static ssm_status copy_step_impl(Handle *H, int32_t batch, const int32_t *h_slot_ids,
+                                 int32_t n_in, const void *x, const void *dt, const void *beta,
+                                 const void *B, const void *C, void *y, void *stream) {
   if (!H->copies) return fail(SSM_E_LOG, "copy: no buffer attached");
   if (n_in < 1 || n_in > H->n_in_max)
     return fail(SSM_E_INVALID_ARG, "copy: n_in must be in [1, %d]", H->n_in_max);
@@ -1003,8 +1043,11 @@ ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
   hipStream_t s = as_stream(stream);
   const Dims &d = H->d;
   const size_t nt = (size_t)batch * n_in;
+  const bool gdn = H->rec == SSM_GATED_DELTA;
+  if (gdn && (!beta || !aligned(beta, io_size(H->io))))
+    return fail(SSM_E_INVALID_ARG, "copy: beta is NULL or misaligned");
   st = check_finite(H, s, {{x, nt * d.H * d.P}, {dt, nt * d.H}, {B, nt * d.G * d.N},
-                           {C, nt * d.G * d.N}});
+                           {C, nt * d.G * d.N}, {gdn ? beta : nullptr, gdn ? nt * d.H : 0}});
   if (st != SSM_OK) return st;
   const size_t es = io_size(H->io);
   for (int i0 = 0; i0 < batch; i0 += kBatchPerLaunch) {
@@ -1018,6 +1061,7 @@ ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
     CopyArgs a{};
     a.x = (const char *)x + off * d.H * d.P * es;
     a.dt = (const char *)dt + off * d.H * es;
+    a.beta = gdn ? (const char *)beta + off * d.H * es : nullptr;
     a.B = (const char *)B + off * d.G * d.N * es;
     a.C = (const char *)C + off * d.G * d.N * es;
     a.y = (char *)y + off * d.H * d.P * es;
@@ -1029,7 +1073,10 @@ ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
     a.n = n;
     a.n_in = n_in;
     a.n_in_max = H->n_in_max;
-    HIP_TRY(launch_copy(H->io, a, m, s));
+    if (gdn)
+      HIP_TRY(launch_gdn_copy(H->io, a, m, s));
+    else
+      HIP_TRY(launch_copy(H->io, a, m, s));
   }
   for (int i = 0; i < batch; ++i) {
     Slot &sl = H->slots[h_slot_ids[i]];
@@ -1040,6 +1087,22 @@ ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
   }
   H->cnt.copy_steps++;
   return SSM_OK;
+}
+
+ssm_status ssm_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                         const void *x, const void *dt, const void *B, const void *C, void *y,
+                         void *stream) {
+  GET_HANDLE(H, h);
+  if (ssm_status st = need_rec(H, SSM_MAMBA2, "copy"); st != SSM_OK) return st;
+  return copy_step_impl(H, batch, h_slot_ids, n_in, x, dt, nullptr, B, C, y, stream);
+}
+
+ssm_status ssm_gdn_copy_step(ssm_handle h, int32_t batch, const int32_t *h_slot_ids, int32_t n_in,
+                             const void *v, const void *dt, const void *beta, const void *k,
+                             const void *q, void *y, void *stream) {
+  GET_HANDLE(H, h);
+  if (ssm_status st = need_rec(H, SSM_GATED_DELTA, "gdn copy"); st != SSM_OK) return st;
+  return copy_step_impl(H, batch, h_slot_ids, n_in, v, dt, beta, k, q, y, stream);
 }
 
 ssm_status ssm_copy_commit(ssm_handle h, int32_t batch, const int32_t *h_slot_ids,
@@ -1101,6 +1164,7 @@ namespace {
 // A receipt field that does not match the handle, or nullptr.
 static const char *receipt_mismatch(const Handle *H, const ssm_receipt *r) {
   if (r->schema_version != H->desc.schema_version) return "schema version";
+  if (r->recurrence != (uint32_t)H->rec) return "recurrence";
   if (r->state_dtype != SSM_F32) return "state dtype";
   if (r->H != H->d.H || r->P != H->d.P || r->N != H->d.N || r->G != H->d.G) return "dimensions";
   if (r->model_rev != H->desc.model_rev) return "model revision";

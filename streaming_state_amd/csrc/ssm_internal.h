@@ -58,6 +58,7 @@ struct CopyMeta {
 };
 struct CopyArgs {
   const void *x, *dt, *B, *C;  // [n, n_in, ...] for this launch
+  const void *beta;            // Gated DeltaNet: [n, n_in, H]
   void *y;
   const float *state;
   float *copies;  // [S, n_in_max, H, P, N]
@@ -66,6 +67,8 @@ struct CopyArgs {
   int n, n_in, n_in_max;
 };
 hipError_t launch_copy(int io, const CopyArgs &a, const CopyMeta &m, hipStream_t s);
+// The same baseline for the Gated DeltaNet recurrence (x = v, B = k, C = q).
+hipError_t launch_gdn_copy(int io, const CopyArgs &a, const CopyMeta &m, hipStream_t s);
 
 // ------------------------------------------------------------------ replay
 // Per entry: the slot and one 32-bit word (read through the scalar cache) with
@@ -93,6 +96,7 @@ __host__ __device__ inline uint32_t fastdiv_magic(int d) {
 
 struct ReplayArgs {
   const void *x, *dt, *B, *C;  // [n, n_in, ...] for this launch
+  const void *beta;            // Gated DeltaNet: [n, n_in, H]
   void *y;
   float *state;                // checkpoints [S, H, P, N]
   void *log;                   // [S][2][W] entries (see log_offsets)
@@ -102,14 +106,19 @@ struct ReplayArgs {
   int n, n_in, W;
   uint32_t nin_magic;          // fastdiv_magic(n_in)
 };
-// Log layout: three arrays, each [S][2 halves][W entries][...] in the io dtype
-// (dt: [H], x: [H*P], B: [G*N]), then fp32 B.C scratch.
+// Log layout: arrays of [S][2 halves][W entries][...] in the io dtype (dt:
+// [H], x: [H*P], B: [G*N]; Gated DeltaNet also beta: [H]), then for Mamba-2
+// the fp32 B.C scratch.
 struct LogLayout {
-  size_t dt_off, x_off, B_off, bc_off, total;  // byte offsets
+  size_t dt_off, beta_off, x_off, B_off, bc_off, total;  // byte offsets
 };
-LogLayout log_layout(int io, const Dims &d, int S, int W);
+LogLayout log_layout(int io, const Dims &d, int S, int W, bool gdn);
 hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const LogLayout &lay,
                          hipStream_t s);
+// ReplaySSM verify of the Gated DeltaNet recurrence (x = v, B = k, C = q):
+// the same metadata and log halves, the gated delta rule for the fold.
+hipError_t launch_gdn_replay(int io, const ReplayArgs &a, const ReplayMeta &m,
+                             const LogLayout &lay, hipStream_t s);
 
 // -------------------------------------------------------------------- scan
 struct ScanSeg {

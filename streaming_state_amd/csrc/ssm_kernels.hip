@@ -93,16 +93,18 @@ hipError_t launch_copy(int io, const CopyArgs &a, const CopyMeta &m, hipStream_t
 // Log of one slot: two halves of W entries each.  A fold (flush) reads the
 // half that holds the committed entries while the step's in-flight entries
 // are appended to the other half, so the two never overlap within a launch.
-LogLayout log_layout(int io, const Dims &d, int S, int W) {
+LogLayout log_layout(int io, const Dims &d, int S, int W, bool gdn) {
   const size_t es = io == kBF16 ? 2 : 4;
   const size_t ent = (size_t)S * 2 * W;
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
   LogLayout L;
   L.dt_off = 0;
-  L.x_off = (L.dt_off + ent * d.H * es + 255) & ~(size_t)255;
-  L.B_off = (L.x_off + ent * d.H * d.P * es + 255) & ~(size_t)255;
-  L.bc_off = (L.B_off + ent * d.G * d.N * es + 255) & ~(size_t)255;
-  // B.C scratch: [kBatchPerLaunch][G][W][kMaxInFlight] fp32
-  L.total = L.bc_off + (size_t)kBatchPerLaunch * d.G * W * kMaxInFlight * 4;
+  L.beta_off = up(L.dt_off + ent * d.H * es);
+  L.x_off = gdn ? up(L.beta_off + ent * d.H * es) : L.beta_off;  // beta: Gated DeltaNet only
+  L.B_off = up(L.x_off + ent * d.H * d.P * es);
+  L.bc_off = up(L.B_off + ent * d.G * d.N * es);
+  // Mamba-2's B.C scratch: [kBatchPerLaunch][G][W][kMaxInFlight] fp32
+  L.total = L.bc_off + (gdn ? 0 : (size_t)kBatchPerLaunch * d.G * W * kMaxInFlight * 4);
   return L;
 }
 
@@ -221,55 +223,6 @@ struct ReplaySmem {
     total = dot + 4 * n_in * rows;
   }
 };
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Copy n 16-byte chunks global -> LDS: chunk i lands at lds + 16 i, read from
-// src_of(i).  Each wave instruction fills 64 consecutive chunks (lane l
-// writes 16 bytes at the wave's LDS base + 16 l; inactive lanes write
-// nothing).  The copies complete asynchronously: wait on vmcnt before use.
-template <typename SrcOf>
-__device__ __forceinline__ void stage_lds(char *lds, int n, SrcOf src_of) {
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  for (int blk = wave; blk * 64 < n; blk += kThreads / 64) {
-    const int i = blk * 64 + lane;
-    if (i < n)
-      __builtin_amdgcn_global_load_lds(src_of(i), (lds_void_t *)(lds + blk * 1024), 16, 0, 0);
-  }
-}
-
-template <typename T> __device__ __forceinline__ float4 lds_ld4(const T *p);
-template <> __device__ __forceinline__ float4 lds_ld4<float>(const float *p) {
-  return *reinterpret_cast<const float4 *>(p);
-}
-template <> __device__ __forceinline__ float4 lds_ld4<bf16_t>(const bf16_t *p) {
-  const uint2 r = *reinterpret_cast<const uint2 *>(p);
-  return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
-}
-
-// R consecutive io values from LDS (16-byte aligned) as floats.
-template <typename T, int R> __device__ __forceinline__ void lds_ld_rows(const T *p, float *v) {
-  static_assert((R * sizeof(T)) % 16 == 0, "whole 16-byte reads");
-#pragma unroll
-  for (int q = 0; q < (int)(R * sizeof(T)) / 16; ++q) {
-    const uint4 u = reinterpret_cast<const uint4 *>(p)[q];
-    if (sizeof(T) == 4) {
-      v[4 * q + 0] = __uint_as_float(u.x);
-      v[4 * q + 1] = __uint_as_float(u.y);
-      v[4 * q + 2] = __uint_as_float(u.z);
-      v[4 * q + 3] = __uint_as_float(u.w);
-    } else {
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[8 * q + 2 * t] = __uint_as_float(w[t] << 16);
-        v[8 * q + 2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
-      }
-    }
-  }
-}
 
 // Eight waves per SIMD (<= 64 VGPRs): eight workgroups, 256 KiB of checkpoint
 // loads in flight per CU.  kFull: every tile has 64 rows inside the head and

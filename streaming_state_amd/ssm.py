@@ -51,6 +51,7 @@ SSM_E_SCHEMA = -5
 SSM_E_LOG = -6
 SSM_E_HIP = -7
 SSM_F32, SSM_F16, SSM_BF16 = 0, 1, 2
+SSM_MAMBA2, SSM_GATED_DELTA = 0, 1
 SSM_FLAG_CHECK_FINITE = 1
 SSM_STATIC_WORKSPACE_BYTES = 16 << 20
 
@@ -62,7 +63,8 @@ _NAMES = {0: "SSM_OK", -1: "SSM_E_INVALID_ARG", -2: "SSM_E_INVALID_CHUNK",
 class LayerDesc(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("P", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("G", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
-                ("schema_version", ctypes.c_uint32), ("model_rev", ctypes.c_uint64)]
+                ("schema_version", ctypes.c_uint32), ("model_rev", ctypes.c_uint64),
+                ("recurrence", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Receipt(ctypes.Structure):
@@ -70,16 +72,18 @@ class Receipt(ctypes.Structure):
                 ("code_rev", ctypes.c_uint64), ("schema_version", ctypes.c_uint32),
                 ("state_dtype", ctypes.c_uint32), ("H", ctypes.c_int32), ("P", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("G", ctypes.c_int32), ("position", ctypes.c_int64),
-                ("chunk_seq", ctypes.c_uint64), ("checksum", ctypes.c_uint64)]
+                ("chunk_seq", ctypes.c_uint64), ("checksum", ctypes.c_uint64),
+                ("recurrence", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
     def as_dict(self):
-        return {f: getattr(self, f) for f, _ in self._fields_}
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
 
     @classmethod
     def from_dict(cls, d):
+        """Fields missing from d (recurrence, reserved) are 0."""
         r = cls()
         for f, _ in cls._fields_:
-            setattr(r, f, d[f])
+            setattr(r, f, d.get(f, 0))
         return r
 
 
@@ -112,6 +116,8 @@ _SIGS = {
     "ssm_replay_attach": [_H, _I32, _V, _SZ],
     "ssm_replay_step": [_H, _I32, _V, _I32, _V, _V, _V, _V, _V, _V],
     "ssm_replay_commit": [_H, _I32, _V, _V],
+    "ssm_gdn_replay_step": [_H, _I32, _V, _I32, _V, _V, _V, _V, _V, _V, _V],
+    "ssm_gdn_copy_step": [_H, _I32, _V, _I32, _V, _V, _V, _V, _V, _V, _V],
     "ssm_copy_buffer_bytes": [ctypes.POINTER(LayerDesc), _I32, _I32],
     "ssm_copy_attach": [_H, _I32, _V, _SZ],
     "ssm_copy_step": [_H, _I32, _V, _I32, _V, _V, _V, _V, _V, _V],
@@ -233,12 +239,13 @@ class StreamState:
     device tensors that must outlive the handle."""
 
     def __init__(self, H, P, N, n_slots, A, D, G=1, io_dtype="f32", state=None,
-                 check_finite=False, schema_version=1, model_rev=0):
+                 check_finite=False, schema_version=1, model_rev=0, recurrence="mamba2"):
         torch = _torch()
         self.io = {"f32": SSM_F32, "fp32": SSM_F32, "bf16": SSM_BF16}[io_dtype]
         self.io_dtype = _io_torch_dtype(self.io)
         self.H, self.P, self.N, self.G, self.S = H, P, N, G, n_slots
-        self.desc = LayerDesc(H, P, N, G, self.io, schema_version, model_rev)
+        self.rec = {"mamba2": SSM_MAMBA2, "gated_delta": SSM_GATED_DELTA}[recurrence]
+        self.desc = LayerDesc(H, P, N, G, self.io, schema_version, model_rev, self.rec, 0)
         if state is None:
             state = torch.zeros((n_slots, H, P, N), dtype=torch.float32, device="cuda")
         self.state = state
@@ -248,7 +255,8 @@ class StreamState:
         _check(_lib.ssm_create(ctypes.byref(self.desc), n_slots,
                                _dev_ptr(state, torch.float32, (n_slots, H, P, N), "state"),
                                _dev_ptr(A, torch.float32, (H,), "A"),
-                               _dev_ptr(D, torch.float32, (H,), "D"), flags, ctypes.byref(h)))
+                               None if D is None else _dev_ptr(D, torch.float32, (H,), "D"),
+                               flags, ctypes.byref(h)))
         self.handle = h.value
         self.log = None
         self.copies = None
@@ -422,6 +430,30 @@ class StreamState:
             _dev_ptr(C, dt_, (b, n_in, G, N), "C"), _dev_ptr(y, dt_, (b, n_in, H, P), "y"),
             _stream(stream)))
         return y
+
+    def _gdn_step(self, fn, slot_ids, v, dt, beta, k, q, y, stream):
+        torch = _torch()
+        ids, ip = _host(slot_ids, np.int32)
+        b = len(ids)
+        n_in = v.shape[1]
+        H, P, N, G = self.H, self.P, self.N, self.G
+        if y is None:
+            y = torch.empty((b, n_in, H, P), dtype=self.io_dtype, device=v.device)
+        dt_ = self.io_dtype
+        _check(fn(self.handle, b, ip, n_in, _dev_ptr(v, dt_, (b, n_in, H, P), "v"),
+                  _dev_ptr(dt, dt_, (b, n_in, H), "dt"), _dev_ptr(beta, dt_, (b, n_in, H), "beta"),
+                  _dev_ptr(k, dt_, (b, n_in, G, N), "k"), _dev_ptr(q, dt_, (b, n_in, G, N), "q"),
+                  _dev_ptr(y, dt_, (b, n_in, H, P), "y"), _stream(stream)))
+        return y
+
+    def gdn_replay_step(self, slot_ids, v, dt, beta, k, q, y=None, stream=None):
+        """ReplaySSM verify of a Gated DeltaNet handle: v[b,n_in,H,P],
+        dt/beta[b,n_in,H], k/q[b,n_in,G,N]; returns o[b,n_in,H,P]."""
+        return self._gdn_step(_lib.ssm_gdn_replay_step, slot_ids, v, dt, beta, k, q, y, stream)
+
+    def gdn_copy_step(self, slot_ids, v, dt, beta, k, q, y=None, stream=None):
+        """The copy-state-per-draft baseline of gdn_replay_step."""
+        return self._gdn_step(_lib.ssm_gdn_copy_step, slot_ids, v, dt, beta, k, q, y, stream)
 
     def replay_commit(self, slot_ids, accepted):
         ids, ip = _host(slot_ids, np.int32)

@@ -320,3 +320,43 @@ def test_scan_packed_rejects_on_the_host():
     for s_ in range(4):
         assert meta(s_)[0] == 0
     lib.ssm_destroy(h)
+
+
+def test_recurrence_guards_on_the_host():
+    """Gated DeltaNet handles: D may be NULL (Mamba-2 needs it); each
+    recurrence's calls refuse the other's handles; a receipt of the other
+    recurrence is refused; an unknown recurrence is refused."""
+    lib = ssm.lib()
+    g = _desc(H=4, P=8, N=16)
+    g.recurrence = ssm.SSM_GATED_DELTA
+    h = ctypes.c_int64(0)
+    assert lib.ssm_create(ctypes.byref(g), 2, FAKE, FAKE, None, 0, ctypes.byref(h)) == ssm.SSM_OK
+    hm = ctypes.c_int64(0)
+    assert lib.ssm_create(ctypes.byref(_desc()), 2, FAKE, FAKE, None, 0,
+                          ctypes.byref(hm)) == ssm.SSM_E_INVALID_ARG
+    rc, hm = _create()
+    bad = _desc()
+    bad.recurrence = 7
+    assert lib.ssm_create(ctypes.byref(bad), 2, FAKE, FAKE, FAKE, 0,
+                          ctypes.byref(ctypes.c_int64(0))) == ssm.SSM_E_INVALID_ARG
+    ids = (ctypes.c_int32 * 1)(0)
+    assert lib.ssm_decode_step(h.value, 1, ids, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                               None) == ssm.SSM_E_INVALID_ARG
+    assert "Gated DeltaNet" in _err()
+    assert _scan(h.value, 0, 0, 4) == ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_gdn_replay_step(hm, 1, ids, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == ssm.SSM_E_INVALID_ARG
+    assert lib.ssm_gdn_copy_step(hm, 1, ids, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None) == ssm.SSM_E_INVALID_ARG
+    assert "Mamba-2" in _err()
+    # a Gated DeltaNet log holds beta too
+    assert lib.ssm_replay_log_bytes(ctypes.byref(g), 4, 8) != \
+        lib.ssm_replay_log_bytes(ctypes.byref(_desc(H=4, P=8, N=16)), 4, 8)
+    good = dict(stream_id=5, model_rev=77, code_rev=ssm.code_rev(), schema_version=3,
+                state_dtype=0, H=4, P=8, N=16, G=1, position=10, chunk_seq=2, checksum=0,
+                recurrence=ssm.SSM_MAMBA2)
+    r = ssm.Receipt.from_dict(good)
+    assert lib.ssm_state_restore(h.value, 0, FAKE, ctypes.byref(r), None) == ssm.SSM_E_SCHEMA
+    assert "recurrence" in _err()
+    lib.ssm_destroy(h.value)
+    lib.ssm_destroy(hm)
