@@ -128,7 +128,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", default="", help="comma list of decode,replay,copy,prefill,conv (profiling)")
+    ap.add_argument("--only", default="", help="comma list of decode,replay,copy,prefill,conv,gdn (profiling)")
     ap.add_argument("--skip-extras", action="store_true")
     return ap.parse_args()
 
@@ -361,6 +361,8 @@ def main():
     extras = {}
     if "conv" in only:  # the steps around the scan alone (for profiling)
         extras["conv_and_gate"] = conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev)
+    if "gdn" in only:  # Gated DeltaNet verify alone (for profiling)
+        extras["gdn_replay_vs_copy"] = gdn_bench(torch, ssm, inputs, dev)
     if not args.skip_extras and not only:
         # replay at W = 8 and 32 against the same copy baseline
         for W in (8, 32):
@@ -427,6 +429,7 @@ def main():
         extras["stream_130m_abi"] = abi_lat
         extras["replay_alone_vs_decode"] = replay_alone_sweep(torch, ssm, inputs, H, P, N, G, dev)
         extras["conv_and_gate"] = conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev)
+        extras["gdn_replay_vs_copy"] = gdn_bench(torch, ssm, inputs, dev)
         # plain device copy of 1 GiB for the achievable-bandwidth context
         a = torch.empty(256 * MIB, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -586,6 +589,82 @@ def conv_gate_bench(torch, ssm, inputs, H, P, N, G, dev, reps=10):
     ms = timed(lambda: hd.conv_decode(slots, xd, y=yd))
     out["conv_decode_256"] = line(ms, 2 * Bd * C * (K - 1) * 4 + 2 * Bd * C * 4 + C * (K + 1) * 4)
     hd.destroy()
+    return out
+
+
+def gdn_bench(torch, ssm, inputs, dev, steps=48, warm=4, copy_steps=16):
+    """Gated DeltaNet verify at B=256 (32 value heads over 16 key groups,
+    P = N = 128, fp32 state 2 MiB per slot), n_in = 5 (p = 0.7): ReplaySSM at
+    W = 8, 16, 32 against the copy-state-per-draft baseline on the same
+    inputs.  Algorithmic bytes per replay step, from the log lengths: the
+    checkpoint read, the checkpoint write of folding slots, the committed
+    entries read (dt, beta, v, k) and the in-flight ones appended, in-flight
+    inputs and outputs; per copy step: one state read and n_in state writes
+    plus the same inputs and outputs."""
+    w5 = inputs.W5
+    Bd, H, P, N, G, T = w5["batch"], w5["H"], w5["P"], w5["N"], w5["G"], w5["T"]
+    n_in = T + 1
+    A = torch.from_numpy(inputs.params(5, H)[0]).to(dev)
+    init = inputs.device_state(5, Bd, H, P, N)
+    acc = inputs.acceptances(steps + warm, Bd, T=T, p=w5["p"], workload=5)
+    toks = []
+    for s in range(8):
+        v, dt, beta, k, q = inputs.device_gdn_tokens(5, Bd * n_in, H, P, N, G, seed_extra=s)
+        toks.append((v.view(Bd, n_in, H, P), dt.view(Bd, n_in, H), beta.view(Bd, n_in, H),
+                     k.view(Bd, n_in, G, N), q.view(Bd, n_in, G, N)))
+    slots = np.arange(Bd, dtype=np.int32)
+    y = torch.empty((Bd, n_in, H, P), dtype=torch.float32, device=dev)
+    state_b = H * P * N * 4
+    entry_b = (2 * H + H * P + G * N) * 4
+    io_b = n_in * (H * P + 2 * H + 2 * G * N) * 4 + n_in * H * P * 4
+    out = {"batch": Bd, "H": H, "G": G, "P": P, "N": N, "n_in": n_in}
+    c = ssm.StreamState(H, P, N, Bd, A, None, G=G, recurrence="gated_delta")
+    c.init(slots, init)
+    c.copy_attach(n_in)
+    tc = Timer(torch)
+    for s in range(warm + copy_steps):
+        e = tc.start() if s >= warm else None
+        c.gdn_copy_step(slots, *toks[s % len(toks)], y=y)
+        if e is not None:
+            tc.stop(e)
+        c.copy_commit(slots, acc[s])
+    torch.cuda.synchronize()
+    cms = np.array(tc.ms())
+    cbytes = Bd * (state_b * (1 + n_in) + io_b)
+    out["copy"] = dict(ms_mean=float(cms.mean()), bytes_per_step=cbytes,
+                       GBps=cbytes / (cms.mean() * 1e-3) / 1e9,
+                       frac_hbm=cbytes / (cms.mean() * 1e-3) / 8e12)
+    c.destroy()
+    del c
+    for W in (8, 16, 32):
+        r = ssm.StreamState(H, P, N, Bd, A, None, G=G, recurrence="gated_delta")
+        r.init(slots, init)
+        r.replay_attach(W)
+        tm, nbytes = Timer(torch), []
+        for s in range(warm + steps):
+            if s >= warm:
+                tot = 0
+                for b in slots:
+                    ln = r.log_state(int(b))[0]
+                    tot += state_b + (ln + n_in) * entry_b + io_b
+                    if ln + n_in > W:
+                        tot += state_b
+                nbytes.append(tot)
+            e = tm.start() if s >= warm else None
+            r.gdn_replay_step(slots, *toks[s % len(toks)], y=y)
+            if e is not None:
+                tm.stop(e)
+            r.replay_commit(slots, acc[s])
+        torch.cuda.synchronize()
+        ms = np.array(tm.ms())
+        rate = float(np.sum(nbytes) / (ms.sum() * 1e-3))
+        out[f"replay_W{W}"] = dict(ms_mean=float(ms.mean()), bytes_per_step=float(np.mean(nbytes)),
+                                   GBps=rate / 1e9, frac_hbm=rate / 8e12,
+                                   flushes=r.counters()["replay_flushes"],
+                                   speedup_vs_copy=float(cms.mean() / ms.mean()))
+        r.destroy()
+        del r
+    del init, toks
     return out
 
 

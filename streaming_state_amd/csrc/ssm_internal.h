@@ -88,6 +88,12 @@ __host__ __device__ inline int info_fold(uint32_t u) { return (int)(u & 0xffu); 
 __host__ __device__ inline int info_base(uint32_t u) { return (int)((u >> 8) & 0xffu); }
 __host__ __device__ inline int info_fold_half(uint32_t u) { return (int)((u >> 16) & 1u); }
 __host__ __device__ inline int info_live_half(uint32_t u) { return (int)((u >> 17) & 1u); }
+// Bits 18-25: the entry's row in the launch's inputs, outputs and B.C scratch
+// (set by the launcher; a launch may carry a subset of the batch's entries).
+__host__ __device__ inline uint32_t info_with_entry(uint32_t u, int e) {
+  return (u & 0x3ffffu) | (uint32_t)e << 18;
+}
+__host__ __device__ inline int info_entry(uint32_t u) { return (int)((u >> 18) & 0xffu); }
 // Multiplier of the kernels' division by a small divisor d (FastDiv):
 // ceil(2^32 / d) for d > 1.
 __host__ __device__ inline uint32_t fastdiv_magic(int d) {
@@ -105,6 +111,7 @@ struct ReplayArgs {
   Dims d;
   int n, n_in, W;
   uint32_t nin_magic;          // fastdiv_magic(n_in)
+  int vrows, xrows;            // LDS rows reserved for B/C rows and x rows (set by the launcher)
 };
 // Log layout: arrays of [S][2 halves][W entries][...] in the io dtype (dt:
 // [H], x: [H*P], B: [G*N]; Gated DeltaNet also beta: [H]), then for Mamba-2

@@ -199,21 +199,25 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
 constexpr int kReplayR = 8;  // 64-row (32 KiB) tiles
 
 // LDS carve-up of the verify kernel (byte offsets; W window, n_in in-flight
-// tokens, xs = the LDS stride of an entry's x rows (>= rows), rows = the
-// tile's row count, es = io element size):
-//   V [W + n_in][N] io   fold B rows, then in-flight C rows
-//   x [W + n_in][xs] io  combined entries' x, then the fold entries' x
+// tokens, vrows / xrows the rows reserved for the two row regions, xs = the
+// LDS stride of an entry's x rows (>= rows), rows = the tile's row count,
+// es = io element size):
+//   V [vrows][N] io      fold B rows (F), then in-flight C rows (n_in)
+//   x [xrows][xs] io     combined entries' x (J), then the fold entries' x (F)
 //   dt [W], fdt [W], coef [W][n_in] (staged B.C, then the weights),
 //   lam [n_in], fw [W], flam [1], dot [n_in][rows]   (fp32)
-// Combined plus fold entries number at most W + n_in (a step that folds
-// starts its live half empty), so x never runs into dt.
+// A step that folds starts its live half empty (J = n_in), one that does not
+// folds nothing (F = 0): F + n_in and J + F never exceed W + n_in, the most
+// any launch reserves; a launch of entries that do not fold reserves n_in
+// rows of V and its largest J rows of x.
 struct ReplaySmem {
   int V, x, dt, fdt, coef, lam, fw, flam, dot, total;
-  __host__ __device__ ReplaySmem(int W, int n_in, int N, int xs, int rows, int es) {
+  __host__ __device__ ReplaySmem(int W, int n_in, int N, int vrows, int xrows, int xs, int rows,
+                                 int es) {
     auto up16 = [](int b) { return (b + 15) & ~15; };
     V = 0;
-    x = up16(V + (W + n_in) * N * es);
-    dt = up16(x + (W + n_in) * xs * es);
+    x = up16(V + vrows * N * es);
+    dt = up16(x + xrows * xs * es);
     fdt = dt + 4 * W;
     coef = fdt + 4 * W;
     lam = coef + 4 * W * n_in;
@@ -240,9 +244,10 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   const Dims d = a.d;
   const int W = a.W, n_in = a.n_in;
   const int N = kFull ? 4 * 32 : d.N;
-  const int pt = blockIdx.x, h = blockIdx.y, e = blockIdx.z;
-  const int slot = m.slot[e];
-  const uint32_t info = m.info[e];
+  const int pt = blockIdx.x, h = blockIdx.y;
+  const int slot = m.slot[blockIdx.z];
+  const uint32_t info = m.info[blockIdx.z];
+  const int e = info_entry(info);  // row of the launch's inputs and outputs
   const int F = info_fold(info);
   const int base = info_base(info);
   const int rh = info_fold_half(info), wh = info_live_half(info);
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   T *logx = (T *)((char *)a.log + lay.x_off);
   const T *logB = (const T *)((const char *)a.log + lay.B_off);
   const T *inx = (const T *)a.x, *indt = (const T *)a.dt, *inC = (const T *)a.C;
-  const ReplaySmem L(W, n_in, N, xs, rv, (int)sizeof(T));
+  const ReplaySmem L(W, n_in, N, a.vrows, a.xrows, xs, rv, (int)sizeof(T));
   T *s_V = (T *)(sb + L.V);  // [F + n_in][N]
   T *s_x = (T *)(sb + L.x);  // [J + F][xs]
   float *s_dt = (float *)(sb + L.dt), *s_fdt = (float *)(sb + L.fdt);
@@ -430,9 +435,11 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   }
 }
 
-static size_t replay_smem_bytes(int io, int W, int n_in, int N) {
+static size_t replay_smem_bytes(int io, int W, int n_in, int N, int vrows, int xrows) {
   // xs and rows are at most the tile height, so this bounds every tile's need
-  return (size_t)ReplaySmem(W, n_in, N, 8 * kReplayR, 8 * kReplayR, io == kBF16 ? 2 : 4).total;
+  return (size_t)ReplaySmem(W, n_in, N, vrows, xrows, 8 * kReplayR, 8 * kReplayR,
+                            io == kBF16 ? 2 : 4)
+      .total;
 }
 
 static size_t replay_bc_smem_bytes(int W, int n_in, int N) {
@@ -460,18 +467,59 @@ hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const
     if (err != hipSuccess) return err;
   }
   const int pt_n = (a.d.P + 8 * kReplayR - 1) / (8 * kReplayR);
-  dim3 grid(pt_n, a.d.H, a.n), block(kThreads);
-  const size_t sm = replay_smem_bytes(io, a.W, a.n_in, a.d.N);
   const bool full = a.d.P % (8 * kReplayR) == 0 && a.d.N == 4 * 32;
-  auto go = [&](auto kernel) {
-    hipError_t err = allow_lds(kernel, sm);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kernel, grid, block, sm, s, a, m, lay);
-    return hipGetLastError();
+  auto launch = [&](const ReplayArgs &la, const ReplayMeta &lm) {
+    dim3 grid(pt_n, la.d.H, la.n), block(kThreads);
+    const size_t sm = replay_smem_bytes(io, la.W, la.n_in, la.d.N, la.vrows, la.xrows);
+    auto go = [&](auto kernel) {
+      hipError_t err = allow_lds(kernel, sm);
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(kernel, grid, block, sm, s, la, lm, lay);
+      return hipGetLastError();
+    };
+    if (io == kBF16)
+      return full ? go(replay_kernel<bf16_t, kReplayR, true>)
+                  : go(replay_kernel<bf16_t, kReplayR, false>);
+    return full ? go(replay_kernel<float, kReplayR, true>)
+                : go(replay_kernel<float, kReplayR, false>);
   };
-  if (io == kBF16)
-    return full ? go(replay_kernel<bf16_t, kReplayR, true>) : go(replay_kernel<bf16_t, kReplayR, false>);
-  return full ? go(replay_kernel<float, kReplayR, true>) : go(replay_kernel<float, kReplayR, false>);
+  // One launch reserves room for the worst entry (a full fold beside n_in
+  // in-flight tokens).  When that reservation would hold the kernel under
+  // eight workgroups per CU (160 KiB of LDS), the entries that fold go to a
+  // launch of their own and the rest reserve only what they use.
+  const int cap = a.W + a.n_in;
+  const bool split =
+      a.n_in > 0 && replay_smem_bytes(io, a.W, a.n_in, a.d.N, cap, cap) > 160 * 1024 / 8;
+  ReplayMeta mf, mn;
+  int nf = 0, nn = 0, maxF = 0, maxJ = 0;
+  for (int i = 0; i < a.n; ++i) {
+    const uint32_t u = info_with_entry(m.info[i], i);
+    if (split && info_fold(u) == 0) {
+      mn.slot[nn] = m.slot[i];
+      mn.info[nn++] = u;
+      maxJ = max(maxJ, info_base(u) + a.n_in);
+    } else {
+      mf.slot[nf] = m.slot[i];
+      mf.info[nf++] = u;
+      maxF = max(maxF, info_fold(u));
+    }
+  }
+  if (nf > 0) {
+    ReplayArgs la = a;
+    la.n = nf;
+    la.vrows = split ? maxF + a.n_in : cap;
+    la.xrows = la.vrows;
+    hipError_t err = launch(la, mf);
+    if (err != hipSuccess) return err;
+  }
+  if (nn > 0) {
+    ReplayArgs la = a;
+    la.n = nn;
+    la.vrows = a.n_in;
+    la.xrows = maxJ;
+    return launch(la, mn);
+  }
+  return hipSuccess;
 }
 
 // ===========================================================================
