@@ -247,6 +247,22 @@ __device__ __forceinline__ float sum32_dpp(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
   return v;
 }
+// Inclusive prefix sum over the 64 lanes of a wave (lane l gets the sum of
+// lanes 0..l) with DPP lane moves: shifts by 1, 2, 4 and 8 inside each
+// 16-lane row (lanes shifted in from outside the row add 0), then row 0's
+// total into row 1 and row 2's into row 3 (row_bcast:15), then the total of
+// rows 0-1 into rows 2 and 3 (row_bcast:31).  Every partial is a sum of
+// consecutive lanes' values, so nonnegative inputs lose nothing to
+// cancellation.  All 64 lanes must be active.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  SSM_DPP_ADD(v, 0x111);  // row_shr:1
+  SSM_DPP_ADD(v, 0x112);  // row_shr:2
+  SSM_DPP_ADD(v, 0x114);  // row_shr:4
+  SSM_DPP_ADD(v, 0x118);  // row_shr:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return v;
+}
 #undef SSM_DPP_ADD
 
 // Division of an index i < 2^16 by a block-uniform divisor 1 <= d < 2^16:

@@ -94,6 +94,9 @@ __host__ __device__ inline uint32_t info_with_entry(uint32_t u, int e) {
   return (u & 0x3ffffu) | (uint32_t)e << 18;
 }
 __host__ __device__ inline int info_entry(uint32_t u) { return (int)((u >> 18) & 0xffu); }
+// Row stride (floats) of the B.C scratch: one row per in-flight token, the
+// window's entries along it, rounded up to whole 16-byte chunks.
+__host__ __device__ inline int bc_stride(int W) { return (W + 3) & ~3; }
 // Multiplier of the kernels' division by a small divisor d (FastDiv):
 // ceil(2^32 / d) for d > 1.
 __host__ __device__ inline uint32_t fastdiv_magic(int d) {

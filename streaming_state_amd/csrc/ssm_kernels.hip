@@ -103,8 +103,8 @@ LogLayout log_layout(int io, const Dims &d, int S, int W, bool gdn) {
   L.x_off = gdn ? up(L.beta_off + ent * d.H * es) : L.beta_off;  // beta: Gated DeltaNet only
   L.B_off = up(L.x_off + ent * d.H * d.P * es);
   L.bc_off = up(L.B_off + ent * d.G * d.N * es);
-  // Mamba-2's B.C scratch: [kBatchPerLaunch][G][W][kMaxInFlight] fp32
-  L.total = L.bc_off + (gdn ? 0 : (size_t)kBatchPerLaunch * d.G * W * kMaxInFlight * 4);
+  // Mamba-2's B.C scratch: [kBatchPerLaunch][G][kMaxInFlight][bc_stride(W)] fp32
+  L.total = L.bc_off + (gdn ? 0 : (size_t)kBatchPerLaunch * d.G * kMaxInFlight * bc_stride(W) * 4);
   return L;
 }
 
@@ -173,13 +173,14 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
     }
   }
   __syncthreads();
-  float *bc = a.bc + ((size_t)e * d.G + g) * a.W * kMaxInFlight;
+  const int ws = bc_stride(a.W);
+  float *bc = a.bc + ((size_t)e * d.G + g) * kMaxInFlight * ws;
   for (int p = threadIdx.x; p < J * n_in; p += kThreads) {
     const int j = p / n_in, k = p - j * n_in;
     const float4 *bj = sB + j * qs, *ck = sC + k * qs;
     float acc = 0.f;
     for (int t = 0; t < q; ++t) acc += dot4(bj[t], ck[t]);
-    bc[j * kMaxInFlight + k] = acc;
+    bc[k * ws + j] = acc;
   }
 }
 
@@ -201,26 +202,26 @@ constexpr int kReplayR = 8;  // 64-row (32 KiB) tiles
 // LDS carve-up of the verify kernel (byte offsets; W window, n_in in-flight
 // tokens, vrows / xrows the rows reserved for the two row regions, xs = the
 // LDS stride of an entry's x rows (>= rows), rows = the tile's row count,
-// es = io element size):
+// es = io element size, ws = bc_stride(W)):
 //   V [vrows][N] io      fold B rows (F), then in-flight C rows (n_in)
 //   x [xrows][xs] io     combined entries' x (J), then the fold entries' x (F)
-//   dt [W], fdt [W], coef [W][n_in] (staged B.C, then the weights),
-//   lam [n_in], fw [W], flam [1], dot [n_in][rows]   (fp32)
+//   coef [n_in][ws]      staged B.C products, then in place the output weights
+//   dt [W], fdt [W], lam [n_in], fw [W], flam [1], dot [n_in][rows]   (fp32)
 // A step that folds starts its live half empty (J = n_in), one that does not
 // folds nothing (F = 0): F + n_in and J + F never exceed W + n_in, the most
 // any launch reserves; a launch of entries that do not fold reserves n_in
 // rows of V and its largest J rows of x.
 struct ReplaySmem {
-  int V, x, dt, fdt, coef, lam, fw, flam, dot, total;
+  int V, x, coef, dt, fdt, lam, fw, flam, dot, total;
   __host__ __device__ ReplaySmem(int W, int n_in, int N, int vrows, int xrows, int xs, int rows,
                                  int es) {
     auto up16 = [](int b) { return (b + 15) & ~15; };
     V = 0;
     x = up16(V + vrows * N * es);
-    dt = up16(x + xrows * xs * es);
+    coef = up16(x + xrows * xs * es);
+    dt = coef + 4 * n_in * bc_stride(W);
     fdt = dt + 4 * W;
-    coef = fdt + 4 * W;
-    lam = coef + 4 * W * n_in;
+    lam = fdt + 4 * W;
     fw = lam + 4 * n_in;
     flam = fw + 4 * W;
     dot = flam + 4;
@@ -241,8 +242,10 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   const TileR<R, true> tl;
   constexpr int kRows = 8 * R;  // state rows of this workgroup's tile
   constexpr int E = 16 / (int)sizeof(T);  // io elements per 16-byte chunk
+  constexpr int kWaves = kThreads / 64;
   const Dims d = a.d;
   const int W = a.W, n_in = a.n_in;
+  const int ws = bc_stride(W);
   const int N = kFull ? 4 * 32 : d.N;
   const int pt = blockIdx.x, h = blockIdx.y;
   const int slot = m.slot[blockIdx.z];
@@ -271,14 +274,14 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   const ReplaySmem L(W, n_in, N, a.vrows, a.xrows, xs, rv, (int)sizeof(T));
   T *s_V = (T *)(sb + L.V);  // [F + n_in][N]
   T *s_x = (T *)(sb + L.x);  // [J + F][xs]
-  float *s_dt = (float *)(sb + L.dt), *s_fdt = (float *)(sb + L.fdt);
-  float *s_coef = (float *)(sb + L.coef), *s_lam = (float *)(sb + L.lam);
+  float *s_coef = (float *)(sb + L.coef), *s_dt = (float *)(sb + L.dt);
+  float *s_fdt = (float *)(sb + L.fdt), *s_lam = (float *)(sb + L.lam);
   float *s_fw = (float *)(sb + L.fw), *s_flam = (float *)(sb + L.flam);
   float *s_dot = (float *)(sb + L.dot);
 
-  // Five row sources, each a run of rows at a fixed stride: the committed
-  // and the in-flight x, the fold entries' x, the fold B rows and the
-  // in-flight C rows.  Consecutive log entries of a slot and half are
+  // Six row sources, each a run of rows at a fixed stride: the committed
+  // and the in-flight x, the fold entries' x, the fold B rows, the in-flight
+  // C rows and the B.C rows.  Consecutive log entries of a slot and half are
   // consecutive in the log, so every run is (first row, stride, count).
   const size_t xstride = (size_t)d.H * d.P, vstride = (size_t)d.G * N;
   const T *x_com = logx + (li.ent(slot, wh, 0) * d.H + h) * d.P + prow0;
@@ -286,6 +289,8 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   const T *x_fold = logx + (li.ent(slot, rh, 0) * d.H + h) * d.P + prow0;
   const T *b_fold = logB + li.ent(slot, rh, 0) * vstride + (size_t)g * N;
   const T *c_new = inC + (size_t)e * n_in * vstride + (size_t)g * N;
+  const float *bc = a.bc + ((size_t)e * d.G + g) * kMaxInFlight * ws;
+  stage_lds(sb + L.coef, n_in * ws / 4, [&](int i) { return (const void *)(bc + 4 * i); });
   if (whole_chunks) {
     const int cx = rv / E, cv = N / E;
     const FastDiv fx(cx), fv(cv);
@@ -323,63 +328,48 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
     hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * N) : zero4();
   }
 
-  // scalars: combined dt, fold dt, B.C products
-  const float *bc = a.bc + ((size_t)e * d.G + g) * W * kMaxInFlight;
-  const int nS = J + F + J * n_in;
-  const FastDiv fnin(n_in, a.nin_magic);
+  // dt of the combined entries, then of the fold entries: one load per
+  // thread (J + F <= 2 W <= kThreads) and a single wait for everything
   const T *dt_com = logdt + li.ent(slot, wh, 0) * d.H + h;
   const T *dt_new = indt + (size_t)e * n_in * d.H + h;
   const T *dt_fold = logdt + li.ent(slot, rh, 0) * d.H + h;
-  for (int i = threadIdx.x; i < nS; i += kThreads) {
-    if (i < J) {
-      s_dt[i] = to_f(i < base ? dt_com[(size_t)i * d.H] : dt_new[(size_t)(i - base) * d.H]);
-    } else if (i < J + F) {
-      s_fdt[i - J] = to_f(dt_fold[(size_t)(i - J) * d.H]);
-    } else {
-      const int p = i - J - F, j = fnin.div(p), k = p - j * n_in;
-      s_coef[p] = bc[j * kMaxInFlight + k];
-    }
+  const int tid = threadIdx.x;
+  if (tid < J + F) {
+    const T *src = tid < base ? dt_com + (size_t)tid * d.H
+                   : tid < J  ? dt_new + (size_t)(tid - base) * d.H
+                              : dt_fold + (size_t)(tid - J) * d.H;
+    const float v = to_f(*src);
+    if (tid < J)
+      s_dt[tid] = v;
+    else
+      s_fdt[tid - J] = v;
   }
   __builtin_amdgcn_s_waitcnt(0);  // the LDS copies above have landed
   __syncthreads();
 
-  // append the in-flight x and dt to the live log half
-  const FastDiv frows(rv);
-  T *x_app = logx + (li.ent(slot, wh, base) * d.H + h) * d.P + prow0;
-  for (int i = threadIdx.x; i < n_in * rv; i += kThreads) {
-    const int k = frows.div(i), r = i - k * rv;
-    x_app[k * xstride + r] = s_x[(base + k) * xs + r];
-  }
-  if (pt == 0)
-    for (int k = threadIdx.x; k < n_in; k += kThreads)
-      Io<T>::st(logdt + li.ent(slot, wh, base + k) * d.H + h, s_dt[base + k]);
-
-  // scalar weights
-  for (int j = threadIdx.x; j < F; j += kThreads) {
-    float suf = 0.f;
-    for (int i = j + 1; i < F; ++i) suf += s_fdt[i];
-    s_fw[j] = expf(Ah * suf) * s_fdt[j];
-  }
-  if (F > 0 && threadIdx.x == kThreads - 1) {
-    float tot = 0.f;
-    for (int i = 0; i < F; ++i) tot += s_fdt[i];
-    s_flam[0] = expf(Ah * tot);
-  }
-  for (int t = threadIdx.x; t < J * n_in; t += kThreads) {
-    const int j = fnin.div(t), k = t - j * n_in, mm = base + k;
-    float cf = 0.f;
-    if (j <= mm) {
-      float suf = 0.f;
-      for (int i = j + 1; i <= mm; ++i) suf += s_dt[i];
-      cf = expf(Ah * suf) * s_dt[j] * s_coef[t];
-      if (j == mm) cf += Dh;  // the skip term D x_m rides on the newest entry
+  // Scalar weights.  Wave w takes the in-flight tokens w, w + kWaves, ...;
+  // the last wave also the fold.
+  // Lane l stands for entry j = 63 - l, so the lane prefix sum of dt_{j+1}
+  // is the entry suffix sum S_j = sum_{j < i <= m} dt_i (J, F <= W <= 64).
+  const int wave = __builtin_amdgcn_readfirstlane(tl.wave);
+  const int jr = 63 - tl.lane;
+  for (int k = wave; k < n_in; k += kWaves) {
+    const int mm = base + k;
+    const float S = wave_prefix_sum(jr + 1 <= mm ? s_dt[jr + 1] : 0.f);
+    if (jr < ws) {
+      float cf = 0.f;  // zero past the token's own entry
+      if (jr <= mm) {
+        cf = expf(Ah * S) * s_dt[jr] * s_coef[k * ws + jr];
+        if (jr == mm) cf += Dh;  // the skip term D x_m rides on the newest entry
+      }
+      s_coef[k * ws + jr] = cf;
     }
-    s_coef[t] = cf;
+    if (jr == 0) s_lam[k] = expf(Ah * (s_dt[0] + S));
   }
-  for (int k = threadIdx.x; k < n_in; k += kThreads) {
-    float tot = 0.f;
-    for (int i = 0; i <= base + k; ++i) tot += s_dt[i];
-    s_lam[k] = expf(Ah * tot);
+  if (F > 0 && wave == kWaves - 1) {
+    const float S = wave_prefix_sum(jr + 1 < F ? s_fdt[jr + 1] : 0.f);
+    if (jr < F) s_fw[jr] = expf(Ah * S) * s_fdt[jr];
+    if (jr == 0) s_flam[0] = expf(Ah * (s_fdt[0] + S));
   }
   __syncthreads();
 
@@ -417,19 +407,40 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
         s_dot[k * rv + tl.reduced_row()] = v;
     }
   }
+
+  // append the in-flight x and dt to the live log half
+  const FastDiv frows(rv);
+  T *x_app = logx + (li.ent(slot, wh, base) * d.H + h) * d.P + prow0;
+  for (int i = threadIdx.x; i < n_in * rv; i += kThreads) {
+    const int k = frows.div(i), r = i - k * rv;
+    x_app[k * xstride + r] = s_x[(base + k) * xs + r];
+  }
+  if (pt == 0)
+    for (int k = threadIdx.x; k < n_in; k += kThreads)
+      Io<T>::st(logdt + li.ent(slot, wh, base + k) * d.H + h, s_dt[base + k]);
   __syncthreads();
 
   // outputs: lane = row, one wave per in-flight token, so the loop over
-  // entries is uniform across the wave (D x_m is inside coef[m][k])
+  // entries is uniform across the wave (D x_m is inside the newest weight);
+  // the weights of a token are contiguous and read four at a time
   static_assert(kRows == 64, "one lane per tile row");
   if (tl.lane < rv) {
     const int r = tl.lane;
     T *yr = (T *)a.y + ((size_t)e * n_in * d.H + h) * d.P + prow0 + r;
-    for (int k = __builtin_amdgcn_readfirstlane(tl.wave); k < n_in; k += kThreads / 64) {
+    for (int k = wave; k < n_in; k += kWaves) {
       const int mm = base + k;
+      const float *cf = s_coef + k * ws;
+      const T *xr = s_x + r;
       float acc = s_lam[k] * s_dot[k * rv + r];
-#pragma unroll 4
-      for (int j = 0; j <= mm; ++j) acc += s_coef[j * n_in + k] * to_f(s_x[j * xs + r]);
+      int j = 0;
+      for (; j + 3 <= mm; j += 4) {
+        const float4 c = *reinterpret_cast<const float4 *>(cf + j);
+        acc += c.x * to_f(xr[j * xs]);
+        acc += c.y * to_f(xr[(j + 1) * xs]);
+        acc += c.z * to_f(xr[(j + 2) * xs]);
+        acc += c.w * to_f(xr[(j + 3) * xs]);
+      }
+      for (; j <= mm; ++j) acc += cf[j] * to_f(xr[j * xs]);
       Io<T>::st(yr + (size_t)k * d.H * d.P, acc);
     }
   }
