@@ -9,8 +9,10 @@ One bench step is one pass of every path over one batch of synthetic input:
   copy     the copy-state-per-draft baseline of the same verify, then commit
   prefill  one 65,536-token chunk of 8 packed bf16 sequences (H=128, P=64,
            N=128), resets at sequence starts, final states as checkpoints
-Each path is timed with events on the stream it runs on; ``value`` is the
-decode state bandwidth (algorithmic state + input + output bytes per step
+The K timed steps run path by path (K decode steps, then K verify steps, and
+so on: the same work as K interleaved steps), so that every path is timed in
+its own steady state.  Each path is timed with events on the stream it runs
+on; ``value`` is the decode state bandwidth (algorithmic state + input + output bytes per step
 divided by the decode kernel time).  Replay windows 8 and 32, the
 Mamba-130M-shaped chunked streaming layer and the CPU oracle are measured
 beside the steps.  Prints ONE JSON line.
@@ -154,6 +156,34 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs]
 
 
+class LogMirror:
+    """Replay log lengths per slot, mirrored on the host from the accept
+    counts (the library's rule: a step whose committed entries plus its n_in
+    in-flight tokens exceed W folds the log first and restarts it empty), so
+    that a step's algorithmic bytes need no library query between timed
+    launches.  check() compares the mirror with the library afterwards."""
+
+    def __init__(self, n_slots, W, n_in):
+        self.W, self.n_in = W, n_in
+        self.lens = np.zeros(n_slots, np.int64)
+
+    def step_bytes(self, state_b, entry_b, io_b):
+        """Checkpoint read; the committed log read (a fold reads it to fold
+        it, otherwise the outputs read it); on a fold the checkpoint written;
+        the n_in in-flight entries appended; in-flight inputs and outputs."""
+        fold = self.lens + self.n_in > self.W
+        per = state_b + (self.lens + self.n_in) * entry_b + io_b + fold * state_b
+        return int(per.sum())
+
+    def commit(self, acc):
+        fold = self.lens + self.n_in > self.W
+        self.lens = np.where(fold, 0, self.lens) + np.asarray(acc, np.int64)
+
+    def check(self, r):
+        got = np.array([r.log_state(b)[0] for b in range(len(self.lens))])
+        assert (got == self.lens).all(), "log length mirror disagrees with the library"
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -253,66 +283,72 @@ def main():
     entry_b = (H + H * P + G * N) * 4   # one log entry: dt[H], x[H,P], B[G,N]
     io_b = n_in * (2 * H * P + H + 2 * G * N) * 4  # in-flight x, dt, B, C in; y out
 
-    def replay_bytes(r, slots, W):
-        """Checkpoint read; on a fold, the committed log read and the checkpoint
-        written; otherwise the committed log read for the outputs; the n_in
-        in-flight entries appended; in-flight inputs and outputs."""
-        tot = 0
-        for b in slots:
-            ln = r.log_state(int(b))[0]
-            tot += state_b + ln * entry_b + n_in * entry_b + io_b
-            if ln + n_in > W:
-                tot += state_b
-        return tot
+    mir16 = LogMirror(Bd, 16, n_in)
 
-    def one_step(s, timed):
+    # One step runs every path once.  The K timed steps run path by path
+    # (K decode steps, then K verify steps, ...) so that each path is timed in
+    # its own steady state rather than behind another path's memory traffic;
+    # the work timed is the same K passes of every path.
+    def run_decode(s, timed):
         i = s % n_dec_inputs
-        if want("decode"):
-            e = t_dec.start() if timed else None
-            dec.decode_step(dec_slots, *dec_in[i], reset=dec_reset[i], y=y_dec)
-            if timed:
-                t_dec.stop(e)
-                b, sb = dec_bytes(dec_reset[i])
-                step_bytes.append(b)
-                step_state_bytes.append(sb)
+        e = t_dec.start() if timed else None
+        dec.decode_step(dec_slots, *dec_in[i], reset=dec_reset[i], y=y_dec)
+        if timed:
+            t_dec.stop(e)
+            b, sb = dec_bytes(dec_reset[i])
+            step_bytes.append(b)
+            step_state_bytes.append(sb)
+
+    def run_replay(s, timed):
         a = acc_all[s % len(acc_all)]
         sp = spec_in[s % len(spec_in)]
-        if rep16 is not None:
-            # algorithmic bytes of this verify step, from the log lengths
-            rep_bytes_all.append(replay_bytes(rep16, slots3, 16))
-            if timed:
-                rep_bytes.append(rep_bytes_all[-1])
-            e = t_rep.start() if timed else None
-            rep16.replay_step(slots3, *sp, y=y_spec)
-            if timed:
-                t_rep.stop(e)
-            rep16.replay_commit(slots3, a)
-        if cop is not None:
-            e = t_cop.start() if timed else None
-            cop.copy_step(slots3, *sp, y=y_spec)
-            if timed:
-                t_cop.stop(e)
-            cop.copy_commit(slots3, a)
-        if pre is not None:
-            e = t_pre.start() if timed else None
-            # each sequence starts a fresh stream in its own slot; final states
-            # land there and, as checkpoints, in ck4
-            pre.scan_packed(cu4, slots4, d4["x"], d4["dt"], d4["B"], d4["C"], y=y4, final=ck4)
-            if timed:
-                t_pre.stop(e)
+        # algorithmic bytes of this verify step, from the log lengths
+        rep_bytes_all.append(mir16.step_bytes(state_b, entry_b, io_b))
+        if timed:
+            rep_bytes.append(rep_bytes_all[-1])
+        e = t_rep.start() if timed else None
+        rep16.replay_step(slots3, *sp, y=y_spec)
+        if timed:
+            t_rep.stop(e)
+        rep16.replay_commit(slots3, a)
+        mir16.commit(a)
 
-    for s in range(Wm):
-        one_step(s, False)
+    def run_copy(s, timed):
+        a = acc_all[s % len(acc_all)]
+        sp = spec_in[s % len(spec_in)]
+        e = t_cop.start() if timed else None
+        cop.copy_step(slots3, *sp, y=y_spec)
+        if timed:
+            t_cop.stop(e)
+        cop.copy_commit(slots3, a)
+
+    def run_prefill(s, timed):
+        e = t_pre.start() if timed else None
+        # each sequence starts a fresh stream in its own slot; final states
+        # land there and, as checkpoints, in ck4
+        pre.scan_packed(cu4, slots4, d4["x"], d4["dt"], d4["B"], d4["C"], y=y4, final=ck4)
+        if timed:
+            t_pre.stop(e)
+
+    paths = [fn for want_it, fn in ((want("decode"), run_decode), (rep16 is not None, run_replay),
+                                    (cop is not None, run_copy), (pre is not None, run_prefill))
+             if want_it]
+    for fn in paths:
+        for s in range(Wm):
+            fn(s, False)
     torch.cuda.synchronize()
     log(f"warmup {Wm} done")
     if rep16 is not None:
         flushes_before = rep16.counters()["replay_flushes"]
     t0 = time.perf_counter()
-    for s in range(Wm, Wm + K):
-        one_step(s, True)
+    for fn in paths:
+        for s in range(Wm, Wm + K):
+            fn(s, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {K} steps in {wall:.3f} s")
+    if rep16 is not None:
+        mir16.check(rep16)
 
     out = {}
     comp = {}
@@ -370,16 +406,19 @@ def main():
             tm = Timer(torch)
             nst, warm = 48, 4
             wbytes = []
+            mir = LogMirror(Bd, W, n_in)
             for s in range(nst + warm):
                 sp = spec_in[s % len(spec_in)]
                 if s >= warm:
-                    wbytes.append(replay_bytes(r, slots3, W))
+                    wbytes.append(mir.step_bytes(state_b, entry_b, io_b))
                 e = tm.start() if s >= warm else None
                 r.replay_step(slots3, *sp, y=y_spec)
                 if s >= warm:
                     tm.stop(e)
                 r.replay_commit(slots3, acc_all[s])
+                mir.commit(acc_all[s])
             torch.cuda.synchronize()
+            mir.check(r)
             wms = np.array(tm.ms())
             ms = float(wms.mean())
             rate = float(np.sum(wbytes) / (wms.sum() * 1e-3))
@@ -641,21 +680,18 @@ def gdn_bench(torch, ssm, inputs, dev, steps=48, warm=4, copy_steps=16):
         r.init(slots, init)
         r.replay_attach(W)
         tm, nbytes = Timer(torch), []
+        mir = LogMirror(Bd, W, n_in)
         for s in range(warm + steps):
             if s >= warm:
-                tot = 0
-                for b in slots:
-                    ln = r.log_state(int(b))[0]
-                    tot += state_b + (ln + n_in) * entry_b + io_b
-                    if ln + n_in > W:
-                        tot += state_b
-                nbytes.append(tot)
+                nbytes.append(mir.step_bytes(state_b, entry_b, io_b))
             e = tm.start() if s >= warm else None
             r.gdn_replay_step(slots, *toks[s % len(toks)], y=y)
             if e is not None:
                 tm.stop(e)
             r.replay_commit(slots, acc[s])
+            mir.commit(acc[s])
         torch.cuda.synchronize()
+        mir.check(r)
         ms = np.array(tm.ms())
         rate = float(np.sum(nbytes) / (ms.sum() * 1e-3))
         out[f"replay_W{W}"] = dict(ms_mean=float(ms.mean()), bytes_per_step=float(np.mean(nbytes)),

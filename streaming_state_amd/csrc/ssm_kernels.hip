@@ -199,18 +199,56 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
 // LDS and registers.
 constexpr int kReplayR = 8;  // 64-row (32 KiB) tiles
 
+// Register tile of the verify kernel: a workgroup's four waves own 64 state
+// rows; lane l of wave w owns rows 16 w + 2 (l >> 3) + {0, 1} and, of each,
+// the four 16-byte column chunks 32 q + 4 (l & 7), q = 0..3 (8 float4).  A
+// wave load instruction then reads eight whole 128-byte lines, and the total
+// of a row needs only the eight lanes of its group: one mirrored exchange
+// that leaves each lane one of its two rows, then two sums inside quads.
+struct ReplayTile {
+  int lane, wave, c, rg;
+  __device__ __forceinline__ ReplayTile() {
+    lane = threadIdx.x & 63;
+    wave = (threadIdx.x >> 6) & 3;
+    c = lane & 7;
+    rg = lane >> 3;
+  }
+  __device__ __forceinline__ int row(int i) const { return 16 * wave + 2 * rg + i; }
+  __device__ __forceinline__ int col(int q) const { return 32 * q + 4 * c; }
+  // after totals(): the row whose total this lane holds, and one writer per total
+  __device__ __forceinline__ int reduced_row() const { return row((lane >> 2) & 1); }
+  __device__ __forceinline__ bool reduced_writer() const { return (lane & 3) == 0; }
+  __device__ __forceinline__ float totals(float p0, float p1) const {
+    float s = halve_mirror<kDppRowHalfMirror>(p0, p1, (lane >> 2) & 1);
+    s += dpp_f<kDppQuadXor2>(s);
+    s += dpp_f<kDppQuadXor1>(s);
+    return s;
+  }
+};
+
+// Two consecutive io values from LDS (8-byte aligned for fp32, 4 for bf16).
+__device__ __forceinline__ void lds_ld_pair(const float *p, float v[2]) {
+  const float2 u = *reinterpret_cast<const float2 *>(p);
+  v[0] = u.x;
+  v[1] = u.y;
+}
+__device__ __forceinline__ void lds_ld_pair(const bf16_t *p, float v[2]) {
+  const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+  v[0] = __uint_as_float(u << 16);
+  v[1] = __uint_as_float(u & 0xffff0000u);
+}
+
 // LDS carve-up of the verify kernel (byte offsets; W window, n_in in-flight
 // tokens, vrows / xrows the rows reserved for the two row regions, xs = the
 // LDS stride of an entry's x rows (>= rows), rows = the tile's row count,
 // es = io element size, ws = bc_stride(W)):
-//   V [vrows][N] io      fold B rows (F), then in-flight C rows (n_in)
-//   x [xrows][xs] io     combined entries' x (J), then the fold entries' x (F)
+//   V [vrows][N] io      fold B rows (FR = vrows - n_in at a time), then the
+//                        in-flight C rows (n_in)
+//   x [xrows][xs] io     combined entries' x (J), then the fold rows' x (FR)
 //   coef [n_in][ws]      staged B.C products, then in place the output weights
 //   dt [W], fdt [W], lam [n_in], fw [W], flam [1], dot [n_in][rows]   (fp32)
 // A step that folds starts its live half empty (J = n_in), one that does not
-// folds nothing (F = 0): F + n_in and J + F never exceed W + n_in, the most
-// any launch reserves; a launch of entries that do not fold reserves n_in
-// rows of V and its largest J rows of x.
+// folds nothing (F = 0), so xrows = max(W, n_in + FR) covers both.
 struct ReplaySmem {
   int V, x, coef, dt, fdt, lam, fw, flam, dot, total;
   __host__ __device__ ReplaySmem(int W, int n_in, int N, int vrows, int xrows, int xs, int rows,
@@ -232,15 +270,17 @@ struct ReplaySmem {
 // Eight waves per SIMD (<= 64 VGPRs): eight workgroups, 256 KiB of checkpoint
 // loads in flight per CU.  kFull: every tile has 64 rows inside the head and
 // N = 128, so every lane owns rows and columns and the fold and the dot
-// products need no per-lane predicates (a separate instantiation keeps the
-// register budget of each).
+// products need no per-lane predicates; the instantiation for ragged tiles
+// carries those predicates and is given twice the registers (four waves per
+// SIMD) rather than spill.
 template <typename T, int R, bool kFull>
-__global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, ReplayMeta m,
+__global__ __launch_bounds__(kThreads, kFull ? 8 : 4) void replay_kernel(ReplayArgs a, ReplayMeta m,
                                                           LogLayout lay) {
   extern __shared__ float4 rp_smem4[];
   char *sb = reinterpret_cast<char *>(rp_smem4);
-  const TileR<R, true> tl;
-  constexpr int kRows = 8 * R;  // state rows of this workgroup's tile
+  static_assert(R == 8, "two rows of four 16-byte chunks per lane");
+  const ReplayTile tl;
+  constexpr int kRows = 64;  // state rows of this workgroup's tile
   constexpr int E = 16 / (int)sizeof(T);  // io elements per 16-byte chunk
   constexpr int kWaves = kThreads / 64;
   const Dims d = a.d;
@@ -263,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   // LDS stride of an entry's x rows: rv for whole chunks (the copies are
   // contiguous), else rounded up so that every 8-row group starts 16-byte aligned
   const int xs = whole_chunks ? rv : (rv + 7) & ~7;
-  const bool colok = 4 * tl.c < N;
+  auto colok = [&](int q) { return kFull || tl.col(q) < N; };
   const size_t PN = (size_t)d.P * N;
   const float Ah = a.A[h], Dh = a.D[h];
   const LogIdx li{W};
@@ -286,47 +326,66 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   const size_t xstride = (size_t)d.H * d.P, vstride = (size_t)d.G * N;
   const T *x_com = logx + (li.ent(slot, wh, 0) * d.H + h) * d.P + prow0;
   const T *x_new = inx + ((size_t)e * n_in * d.H + h) * d.P + prow0;
-  const T *x_fold = logx + (li.ent(slot, rh, 0) * d.H + h) * d.P + prow0;
-  const T *b_fold = logB + li.ent(slot, rh, 0) * vstride + (size_t)g * N;
   const T *c_new = inC + (size_t)e * n_in * vstride + (size_t)g * N;
   const float *bc = a.bc + ((size_t)e * d.G + g) * kMaxInFlight * ws;
   stage_lds(sb + L.coef, n_in * ws / 4, [&](int i) { return (const void *)(bc + 4 * i); });
+  // Fold entries are staged FR at a time (the rows the launch reserved for
+  // them): the first chunk with everything else, later chunks in the fold.
+  const int FR = a.vrows - n_in;
+  const int es = (int)sizeof(T);
+  const int cx = rv / E, cv = N / E;
+  const FastDiv fx(cx), fv(cv), frv(rv), fn(N);
+  auto run = [&](char *lds, const T *src, size_t stride, int rows, int chunks, FastDiv f) {
+    stage_lds(lds, rows * chunks, [&](int i) {
+      const int j = f.div(i);
+      return (const void *)(src + j * stride + (i - j * chunks) * E);
+    });
+  };
+  // rows not made of aligned 16-byte chunks: element copies
+  auto copy_rows = [&](T *dst, int dpitch, const T *src, size_t stride, int rows, int len,
+                       FastDiv f) {
+    for (int i = threadIdx.x; i < rows * len; i += kThreads) {
+      const int j = f.div(i), r = i - j * len;
+      dst[j * dpitch + r] = src[j * stride + r];
+    }
+  };
+  // fold entries c0 .. c0 + cnt - 1: x rows after the J combined rows, B rows
+  // at the top of V
+  auto stage_fold = [&](int c0, int cnt) {
+    // (sources recomputed here rather than kept live across the fold)
+    const size_t ec = li.ent(slot, rh, c0);
+    const T *xf = logx + (ec * d.H + h) * d.P + prow0;
+    const T *bf = logB + ec * vstride + (size_t)g * N;
+    if (whole_chunks) {
+      run(sb + L.x + J * xs * es, xf, xstride, cnt, cx, fx);
+      run(sb + L.V, bf, vstride, cnt, cv, fv);
+    } else {
+      copy_rows(s_x + J * xs, xs, xf, xstride, cnt, rv, frv);
+      copy_rows(s_V, N, bf, vstride, cnt, N, fn);
+    }
+  };
+  T *s_C = s_V + FR * N;  // in-flight C rows, after the fold rows
   if (whole_chunks) {
-    const int cx = rv / E, cv = N / E;
-    const FastDiv fx(cx), fv(cv);
-    auto run = [&](char *lds, const T *src, size_t stride, int rows, int chunks, FastDiv f) {
-      stage_lds(lds, rows * chunks, [&](int i) {
-        const int j = f.div(i);
-        return (const void *)(src + j * stride + (i - j * chunks) * E);
-      });
-    };
     run(sb + L.x, x_com, xstride, base, cx, fx);
-    run(sb + L.x + base * xs * (int)sizeof(T), x_new, xstride, n_in, cx, fx);
-    run(sb + L.x + J * xs * (int)sizeof(T), x_fold, xstride, F, cx, fx);
-    run(sb + L.V, b_fold, vstride, F, cv, fv);
-    run(sb + L.V + F * N * (int)sizeof(T), c_new, vstride, n_in, cv, fv);
-  } else {  // rows not made of aligned 16-byte chunks: element copies
-    const FastDiv frv(rv), fn(N);
-    for (int i = threadIdx.x; i < (J + F) * rv; i += kThreads) {
-      const int j = frv.div(i), r = i - j * rv;
-      const T *src = j >= J ? x_fold + (j - J) * xstride
-                     : j < base ? x_com + j * xstride : x_new + (j - base) * xstride;
-      s_x[j * xs + r] = src[r];
-    }
-    for (int i = threadIdx.x; i < (F + n_in) * N; i += kThreads) {
-      const int r = fn.div(i);
-      s_V[i] = (r < F ? b_fold + r * vstride : c_new + (r - F) * vstride)[i - r * N];
-    }
+    run(sb + L.x + base * xs * es, x_new, xstride, n_in, cx, fx);
+    run((char *)s_C, c_new, vstride, n_in, cv, fv);
+  } else {
+    copy_rows(s_x, xs, x_com, xstride, base, rv, frv);
+    copy_rows(s_x + base * xs, xs, x_new, xstride, n_in, rv, frv);
+    copy_rows(s_C, N, c_new, vstride, n_in, N, fn);
   }
+  stage_fold(0, min(F, FR));
 
   // checkpoint tile
-  float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * N + 4 * tl.c;
-  float4 hv[R];
+  float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * N;
+  float4 hv[R];  // hv[4 i + q]: row(i), chunk q
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const bool ok = colok && (tl.row(i) < rv);
-    hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * N) : zero4();
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = colok(q) && (kFull || tl.row(i) < rv);
+      hv[4 * i + q] = ok ? nt_load4(st + (size_t)tl.row(i) * N + tl.col(q)) : zero4();
+    }
 
   // dt of the combined entries, then of the fold entries: one load per
   // thread (J + F <= 2 W <= kThreads) and a single wait for everything
@@ -374,38 +433,59 @@ __global__ __launch_bounds__(kThreads, 8) void replay_kernel(ReplayArgs a, Repla
   __syncthreads();
 
   // fold, then ckpt . C_k for every in-flight token
-  const T *s_C = s_V + F * N;
-  {
-    const bool ck = kFull || colok;
-    if (F > 0) {
-      const float lam = s_flam[0];
+  if (F > 0) {
+    const float lam = s_flam[0];
 #pragma unroll
-      for (int i = 0; i < R; ++i)
-        hv[i] = make_float4(lam * hv[i].x, lam * hv[i].y, lam * hv[i].z, lam * hv[i].w);
-      const T *fx = s_x + J * xs + tl.row(0);  // this lane's R consecutive rows
-#pragma unroll 1
-      for (int j = 0; j < F; ++j) {
-        const float4 Bv = ck ? lds_ld4(s_V + j * N + 4 * tl.c) : zero4();
-        const float w = s_fw[j];
-        float xv[R];
-        lds_ld_rows<T, R>(fx + j * xs, xv);
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-          hv[i] = fma4(1.f, hv[i], (kFull || tl.row(i) < rv) ? w * xv[i] : 0.f, Bv);
+    for (int i = 0; i < R; ++i)
+      hv[i] = make_float4(lam * hv[i].x, lam * hv[i].y, lam * hv[i].z, lam * hv[i].w);
+    const T *fx = s_x + J * xs + tl.row(0);  // this lane's two consecutive rows
+    for (int c0 = 0; c0 < F; c0 += FR) {  // uniform across the workgroup
+      const int cnt = min(FR, F - c0);
+      if (c0 > 0) {  // the next chunk of fold rows, once every wave is done with this one
+        __syncthreads();
+        stage_fold(c0, cnt);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
       }
+#pragma unroll 1
+      for (int j = 0; j < cnt; ++j) {
+        const float w = s_fw[c0 + j];
+        float xv[2];
+        lds_ld_pair(fx + j * xs, xv);
 #pragma unroll
-      for (int i = 0; i < R; ++i)
-        if (ck && (kFull || tl.row(i) < rv)) nt_store4(st + (size_t)tl.row(i) * N, hv[i]);
-    }
-    for (int k = 0; k < n_in; ++k) {
-      const float4 Cv = ck ? lds_ld4(s_C + k * N + 4 * tl.c) : zero4();
-      float part[R];
+        for (int q = 0; q < 4; ++q) {
+          const float4 Bv = colok(q) ? lds_ld4(s_V + j * N + tl.col(q)) : zero4();
 #pragma unroll
-      for (int i = 0; i < R; ++i) part[i] = dot4(hv[i], Cv);
-      const float v = row_totals<R>(part, tl.lane);
-      if (tl.reduced_writer() && (kFull || tl.reduced_row() < rv))
-        s_dot[k * rv + tl.reduced_row()] = v;
+          for (int i = 0; i < 2; ++i)
+            hv[4 * i + q] =
+                fma4(1.f, hv[4 * i + q], (kFull || tl.row(i) < rv) ? w * xv[i] : 0.f, Bv);
+        }
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (colok(q) && (kFull || tl.row(i) < rv))
+          nt_store4(st + (size_t)tl.row(i) * N + tl.col(q), hv[4 * i + q]);
+  }
+  for (int k = 0; k < n_in; ++k) {
+    float part[2];  // one multiply-add chain per row over the lane's 16 columns
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 Cv = colok(q) ? lds_ld4(s_C + k * N + tl.col(q)) : zero4();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float4 hq = hv[4 * i + q];
+        float acc = q == 0 ? hq.x * Cv.x : fmaf(hq.x, Cv.x, part[i]);
+        acc = fmaf(hq.y, Cv.y, acc);
+        acc = fmaf(hq.z, Cv.z, acc);
+        part[i] = fmaf(hq.w, Cv.w, acc);
+      }
+    }
+    const float v = tl.totals(part[0], part[1]);
+    if (tl.reduced_writer() && (kFull || tl.reduced_row() < rv))
+      s_dot[k * rv + tl.reduced_row()] = v;
   }
 
   // append the in-flight x and dt to the live log half
@@ -494,43 +574,31 @@ hipError_t launch_replay(int io, const ReplayArgs &a, const ReplayMeta &m, const
     return full ? go(replay_kernel<float, kReplayR, true>)
                 : go(replay_kernel<float, kReplayR, false>);
   };
-  // One launch reserves room for the worst entry (a full fold beside n_in
-  // in-flight tokens).  When that reservation would hold the kernel under
-  // eight workgroups per CU (160 KiB of LDS), the entries that fold go to a
-  // launch of their own and the rest reserve only what they use.
-  const int cap = a.W + a.n_in;
-  const bool split =
-      a.n_in > 0 && replay_smem_bytes(io, a.W, a.n_in, a.d.N, cap, cap) > 160 * 1024 / 8;
-  ReplayMeta mf, mn;
-  int nf = 0, nn = 0, maxF = 0, maxJ = 0;
+  // One launch for every entry.  Its LDS reservation holds the in-flight C
+  // rows, the largest J rows of x and FR fold rows (B and x); an entry that
+  // folds more than FR entries stages them FR at a time.  FR is the largest
+  // count whose reservation keeps eight workgroups per CU (160 KiB of LDS),
+  // at least eight (else all of the longest fold at once).
+  ReplayMeta ml;
+  int maxF = 0, maxJ = a.n_in;
   for (int i = 0; i < a.n; ++i) {
     const uint32_t u = info_with_entry(m.info[i], i);
-    if (split && info_fold(u) == 0) {
-      mn.slot[nn] = m.slot[i];
-      mn.info[nn++] = u;
-      maxJ = max(maxJ, info_base(u) + a.n_in);
-    } else {
-      mf.slot[nf] = m.slot[i];
-      mf.info[nf++] = u;
-      maxF = max(maxF, info_fold(u));
-    }
+    ml.slot[i] = m.slot[i];
+    ml.info[i] = u;
+    maxF = max(maxF, info_fold(u));
+    if (info_fold(u) == 0) maxJ = max(maxJ, info_base(u) + a.n_in);
   }
-  if (nf > 0) {
-    ReplayArgs la = a;
-    la.n = nf;
-    la.vrows = split ? maxF + a.n_in : cap;
-    la.xrows = la.vrows;
-    hipError_t err = launch(la, mf);
-    if (err != hipSuccess) return err;
-  }
-  if (nn > 0) {
-    ReplayArgs la = a;
-    la.n = nn;
-    la.vrows = a.n_in;
-    la.xrows = maxJ;
-    return launch(la, mn);
-  }
-  return hipSuccess;
+  if (a.n == 0) return hipSuccess;
+  auto smem = [&](int fr) {
+    return replay_smem_bytes(io, a.W, a.n_in, a.d.N, fr + a.n_in, max(maxJ, a.n_in + fr));
+  };
+  int FR = maxF;
+  while (FR > 8 && smem(FR) > 160 * 1024 / 8) --FR;
+  if (smem(FR) > 160 * 1024 / 8) FR = maxF;
+  ReplayArgs la = a;
+  la.vrows = FR + a.n_in;
+  la.xrows = max(maxJ, a.n_in + FR);
+  return launch(la, ml);
 }
 
 // ===========================================================================
