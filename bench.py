@@ -43,8 +43,8 @@ MIB = 1 << 20
 # figure into null until the counters are taken again.
 DECODE_COUNTERS = {
     "sources": ["ssm_decode.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "ba4a931c0511166a8a83db12b93a7ab301b4be4390f48245464bb7ac97bac047",
-    "fetch_kib": 519889.04, "write_kib": 1056770.55,
+    "sha256": "294efb9df64ee438ee108263de83f9cb94f6bbf1f8f827d9bc4fdf1231239146",
+    "fetch_kib": 519888.66, "write_kib": 1056769.83,
     "calib_fetch_kib": 2059.01, "calib_write_kib": 4096.0, "calib_true_kib": 4096.0,
     "algorithmic_kib": 1035989.33 + 1056768.0,
 }
@@ -56,11 +56,13 @@ DECODE_COUNTERS = {
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
     "sources": ["ssm_ssd_pair.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "56148462b010cb5cf2003408ebbf230eeb08b4b5612289870b8a5d046942fc81",
-    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14312899.17, "xcds": 8, "simds": 1024,
+    "sha256": "831d3afb3f104c030abb9f11309144ef2006b1a5f74222e4e6b9e48e2653de1a",
+    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14487844.50, "xcds": 8, "simds": 1024,
     "mfma_mops_bf16": 722141184.0,
-    "fetch_kib": 721036.72, "write_kib": 1085440.21,
-    "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2**25 + 2 * 2**22,
+    "fetch_kib": 721028.46, "write_kib": 1114112.18,
+    # x in and y out (bf16), dt, B, C (bf16), and each sequence's final state
+    # twice (into its slot and as a checkpoint)
+    "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2 * 2**25,
 }
 
 # The same for replay_kernel at W = 16 (mean over the 6 verify steps of
@@ -68,8 +70,8 @@ PREFILL_COUNTERS = {
 # steps, from the log lengths, averaged).
 REPLAY_COUNTERS = {
     "sources": ["ssm_kernels.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "1bb3c309cd0f6dfc648d54aa21b5f19a80d9b8a44876a16b4610a53020be2b32",
-    "fetch_kib": 577233.12, "write_kib": 208581.34,
+    "sha256": "0c3e151d8851d3b215fc30eff4e83367146f68bea0fcdbb955f9dc8c6f790ffd",
+    "fetch_kib": 577003.95, "write_kib": 208610.13,
     "algorithmic_bytes": 1375888554.67,
 }
 
