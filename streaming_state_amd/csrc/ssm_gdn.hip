@@ -135,16 +135,20 @@ struct GdnSmem {
 };
 
 // One (batch entry, head, 64-row tile) per workgroup; the state tile lives in
-// registers (lane l of wave w: float4 column l & 31 of the 8 consecutive rows
-// 8 (2w + (l >> 5)) + i).  kFull: P a multiple of 64 and N = 128 (no
-// per-lane predicates).
+// registers in the Mamba-2 verify kernel's layout (ReplayTile: two rows of
+// four 16-byte chunks per lane, eight lanes per row).  kFull: P a multiple of
+// 64 and N = 128 (no per-lane predicates); six waves per SIMD for it (at 64
+// registers the sweep and the fold spill), four for the instantiation that
+// carries the predicates.
 template <typename T, int R, bool kFull>
-__global__ __launch_bounds__(kThreads, 4) void gdn_replay_kernel(ReplayArgs a, ReplayMeta m,
-                                                                 LogLayout lay) {
+__global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(ReplayArgs a,
+                                                                            ReplayMeta m,
+                                                                            LogLayout lay) {
   extern __shared__ float4 gd_smem4[];
   char *sb = reinterpret_cast<char *>(gd_smem4);
-  const TileR<R, true> tl;
-  constexpr int kRows = 8 * R;
+  static_assert(R == 8, "two rows of four 16-byte chunks per lane");
+  const ReplayTile tl;
+  constexpr int kRows = 64;
   constexpr int E = 16 / (int)sizeof(T);  // io elements per 16-byte chunk
   constexpr int es = (int)sizeof(T);
   const Dims d = a.d;
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 4) void gdn_replay_kernel(ReplayArgs a, R
   const bool whole_chunks = (d.P * es) % 16 == 0 && (N * es) % 16 == 0 &&
                             (((uintptr_t)a.x | (uintptr_t)a.B | (uintptr_t)a.C) & 15) == 0;
   const int xs = whole_chunks ? rv : (rv + 7) & ~7;
-  const bool colok = 4 * tl.c < N;
+  auto colok = [&](int q) { return kFull || tl.col(q) < N; };
   const size_t PN = (size_t)d.P * N;
   const float Ah = a.A[h];
   const GdnLogIdx li{W};
@@ -227,13 +231,15 @@ __global__ __launch_bounds__(kThreads, 4) void gdn_replay_kernel(ReplayArgs a, R
   }
 
   // checkpoint tile
-  float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * N + 4 * tl.c;
-  float4 hv[R];
+  float *st = a.state + ((size_t)slot * d.H + h) * PN + (size_t)prow0 * N;
+  float4 hv[R];  // hv[4 i + q]: row(i), chunk q
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const bool ok = colok && (tl.row(i) < rv);
-    hv[i] = ok ? nt_load4(st + (size_t)tl.row(i) * N) : gz4();
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = colok(q) && (kFull || tl.row(i) < rv);
+      hv[4 * i + q] = ok ? nt_load4(st + (size_t)tl.row(i) * N + tl.col(q)) : gz4();
+    }
 
   // gates: combined entries (committed, then in-flight) and fold entries
   const T *dt_com = logdt + li.ent(slot, wh, 0) * d.H + h;
@@ -309,36 +315,62 @@ __global__ __launch_bounds__(kThreads, 4) void gdn_replay_kernel(ReplayArgs a, R
   // fold: step the checkpoint through the committed entries of the full half
   // (S <- alpha S + (beta (v - alpha S k)) k^T per entry) and write it back
   if (F > 0) {
-    const T *fx = s_x + J * xs + tl.row(0);  // this lane's R consecutive rows
+    const T *fx = s_x + J * xs + tl.row(0);  // this lane's two consecutive rows
 #pragma unroll 1
     for (int j = 0; j < F; ++j) {
-      const float4 kv = (kFull || colok) ? lds_ld4(s_K + j * N + 4 * tl.c) : gz4();
-      float xv[R];
-      lds_ld_rows<T, R>(fx + j * xs, xv);
+      float4 kq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kq[q] = colok(q) ? lds_ld4(s_K + j * N + tl.col(q)) : gz4();
+      float xv[2];
+      lds_ld_pair(fx + j * xs, xv);
       const float al = s_falpha[j], be = s_fbeta[j];
-      float rd[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) rd[i] = allsum32(dot4(hv[i], kv));
+      for (int i = 0; i < 2; ++i) {
+        // (S k)[row]: this lane's 16 columns, then the row's eight lanes
+        float acc = hv[4 * i].x * kq[0].x;
+        acc = fmaf(hv[4 * i].y, kq[0].y, acc);
+        acc = fmaf(hv[4 * i].z, kq[0].z, acc);
+        acc = fmaf(hv[4 * i].w, kq[0].w, acc);
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
+        for (int q = 1; q < 4; ++q) {
+          acc = fmaf(hv[4 * i + q].x, kq[q].x, acc);
+          acc = fmaf(hv[4 * i + q].y, kq[q].y, acc);
+          acc = fmaf(hv[4 * i + q].z, kq[q].z, acc);
+          acc = fmaf(hv[4 * i + q].w, kq[q].w, acc);
+        }
+        const float rd = ReplayTile::row_sum(acc);
         const float vv = (kFull || tl.row(i) < rv) ? xv[i] : 0.f;
-        hv[i] = fma4(al, hv[i], be * (vv - al * rd[i]), kv);
+        const float u = be * (vv - al * rd);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hv[4 * i + q] = fma4(al, hv[4 * i + q], u, kq[q]);
       }
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-      if ((kFull || colok) && (kFull || tl.row(i) < rv)) nt_store4(st + (size_t)tl.row(i) * N, hv[i]);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (colok(q) && (kFull || tl.row(i) < rv))
+          nt_store4(st + (size_t)tl.row(i) * N + tl.col(q), hv[4 * i + q]);
   }
   __syncthreads();  // u and coef are complete
 
   // checkpoint read-out at every carried-back query
   for (int k = 0; k < n_in; ++k) {
-    const float4 Uv = (kFull || colok) ? *reinterpret_cast<const float4 *>(s_u + k * N + 4 * tl.c)
-                                       : gz4();
-    float part[R];
+    float part[2];  // one multiply-add chain per row over the lane's 16 columns
 #pragma unroll
-    for (int i = 0; i < R; ++i) part[i] = dot4(hv[i], Uv);
-    const float v = row_totals<R>(part, tl.lane);
+    for (int q = 0; q < 4; ++q) {
+      const float4 Uv =
+          colok(q) ? *reinterpret_cast<const float4 *>(s_u + k * N + tl.col(q)) : gz4();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float4 hq = hv[4 * i + q];
+        float acc = q == 0 ? hq.x * Uv.x : fmaf(hq.x, Uv.x, part[i]);
+        acc = fmaf(hq.y, Uv.y, acc);
+        acc = fmaf(hq.z, Uv.z, acc);
+        part[i] = fmaf(hq.w, Uv.w, acc);
+      }
+    }
+    const float v = tl.totals(part[0], part[1]);
     if (tl.reduced_writer() && (kFull || tl.reduced_row() < rv)) s_dot[k * rv + tl.reduced_row()] = v;
   }
   __syncthreads();

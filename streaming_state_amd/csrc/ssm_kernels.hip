@@ -199,45 +199,6 @@ __global__ __launch_bounds__(kThreads) void replay_bc_kernel(ReplayArgs a, Repla
 // LDS and registers.
 constexpr int kReplayR = 8;  // 64-row (32 KiB) tiles
 
-// Register tile of the verify kernel: a workgroup's four waves own 64 state
-// rows; lane l of wave w owns rows 16 w + 2 (l >> 3) + {0, 1} and, of each,
-// the four 16-byte column chunks 32 q + 4 (l & 7), q = 0..3 (8 float4).  A
-// wave load instruction then reads eight whole 128-byte lines, and the total
-// of a row needs only the eight lanes of its group: one mirrored exchange
-// that leaves each lane one of its two rows, then two sums inside quads.
-struct ReplayTile {
-  int lane, wave, c, rg;
-  __device__ __forceinline__ ReplayTile() {
-    lane = threadIdx.x & 63;
-    wave = (threadIdx.x >> 6) & 3;
-    c = lane & 7;
-    rg = lane >> 3;
-  }
-  __device__ __forceinline__ int row(int i) const { return 16 * wave + 2 * rg + i; }
-  __device__ __forceinline__ int col(int q) const { return 32 * q + 4 * c; }
-  // after totals(): the row whose total this lane holds, and one writer per total
-  __device__ __forceinline__ int reduced_row() const { return row((lane >> 2) & 1); }
-  __device__ __forceinline__ bool reduced_writer() const { return (lane & 3) == 0; }
-  __device__ __forceinline__ float totals(float p0, float p1) const {
-    float s = halve_mirror<kDppRowHalfMirror>(p0, p1, (lane >> 2) & 1);
-    s += dpp_f<kDppQuadXor2>(s);
-    s += dpp_f<kDppQuadXor1>(s);
-    return s;
-  }
-};
-
-// Two consecutive io values from LDS (8-byte aligned for fp32, 4 for bf16).
-__device__ __forceinline__ void lds_ld_pair(const float *p, float v[2]) {
-  const float2 u = *reinterpret_cast<const float2 *>(p);
-  v[0] = u.x;
-  v[1] = u.y;
-}
-__device__ __forceinline__ void lds_ld_pair(const bf16_t *p, float v[2]) {
-  const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
-  v[0] = __uint_as_float(u << 16);
-  v[1] = __uint_as_float(u & 0xffff0000u);
-}
-
 // LDS carve-up of the verify kernel (byte offsets; W window, n_in in-flight
 // tokens, vrows / xrows the rows reserved for the two row regions, xs = the
 // LDS stride of an entry's x rows (>= rows), rows = the tile's row count,
