@@ -171,6 +171,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
   auto colok = [&](int q) { return kFull || tl.col(q) < N; };
   const size_t PN = (size_t)d.P * N;
   const float Ah = a.A[h];
+  const float Ah2 = Ah * 1.4426950408889634f;  // A in log2 units
   const GdnLogIdx li{W};
   T *logdt = (T *)((char *)a.log + lay.dt_off);
   T *logbeta = (T *)((char *)a.log + lay.beta_off);
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
   T *s_K = (T *)(sb + L.K);
   T *s_x = (T *)(sb + L.x);
   float *s_alpha = (float *)(sb + L.alpha), *s_beta = (float *)(sb + L.beta);
-  float *s_falpha = (float *)(sb + L.falpha), *s_fbeta = (float *)(sb + L.fbeta);
+  float *s_fla = (float *)(sb + L.falpha), *s_fbeta = (float *)(sb + L.fbeta);
   float *s_coef = (float *)(sb + L.coef), *s_u = (float *)(sb + L.u);
   float *s_dot = (float *)(sb + L.dot);
 
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
       s_beta[i] = tofl(com ? be_com[o] : be_new[o]);
     } else {
       const size_t o = (size_t)(i - J) * d.H;
-      s_falpha[i - J] = expf(Ah * tofl(dt_fold[o]));
+      s_fla[i - J] = Ah2 * tofl(dt_fold[o]);
       s_fbeta[i - J] = tofl(be_fold[o]);
     }
   }
@@ -288,34 +289,65 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
     }
   }
 
-  // every in-flight query carried back through the combined entries' factors:
-  // one wave per token, lane l holding elements l and l + 64
+  // every in-flight query carried back through the combined entries' factors,
+  // newest first: two tokens per wave, one per 32-lane half, a lane holding
+  // four consecutive key elements.  The decay stays out of the loop: with the
+  // carried query w = rho * wh, the coefficient is c_j = rho beta_j (k_j . wh),
+  // then wh <- wh - beta_j (k_j . wh) k_j and rho <- alpha_j rho.
   {
-    const int lane = threadIdx.x & 63;
-    const int n0 = lane, n1 = lane + 64;
+    const int half = tl.lane >> 5, n0 = 4 * (tl.lane & 31);
     const T *s_Kc = s_K + F * N, *s_q = s_K + (F + J) * N;
-    for (int k = __builtin_amdgcn_readfirstlane(tl.wave); k < n_in; k += kThreads / 64) {
-      const int mm = base + k;
-      float w0 = n0 < N ? tofl(s_q[k * N + n0]) : 0.f;
-      float w1 = n1 < N ? tofl(s_q[k * N + n1]) : 0.f;
-      for (int j = mm; j >= 0; --j) {
-        const float k0 = n0 < N ? tofl(s_Kc[j * N + n0]) : 0.f;
-        const float k1 = n1 < N ? tofl(s_Kc[j * N + n1]) : 0.f;
-        const float c = s_beta[j] * allsum64(w0 * k0 + w1 * k1);
-        if (lane == 0) s_coef[j * n_in + k] = c;
-        const float al = s_alpha[j];
-        w0 = al * (w0 - c * k0);
-        w1 = al * (w1 - c * k1);
+    auto ld_key4 = [&](const T *row, float v[4]) {
+      if (kFull) {
+        const float4 t = lds_ld4(row + n0);
+        v[0] = t.x;
+        v[1] = t.y;
+        v[2] = t.z;
+        v[3] = t.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = n0 + i < N ? tofl(row[n0 + i]) : 0.f;
       }
-      if (n0 < N) s_u[k * N + n0] = w0;
-      if (n1 < N) s_u[k * N + n1] = w1;
+    };
+    for (int kp = __builtin_amdgcn_readfirstlane(tl.wave); 2 * kp < n_in; kp += kThreads / 64) {
+      const int k = 2 * kp + half;
+      const bool tok = k < n_in;
+      const int mm = base + k;                             // this half's newest entry
+      const int jtop = base + min(2 * kp + 1, n_in - 1);  // the wave's newest entry
+      float w[4] = {0.f, 0.f, 0.f, 0.f};
+      if (tok) ld_key4(s_q + k * N, w);
+      float rho = 1.f;
+      for (int j = jtop; j >= 0; --j) {
+        float kv[4];
+        ld_key4(s_Kc + j * N, kv);
+        float p = w[0] * kv[0];
+        p = fmaf(w[1], kv[1], p);
+        p = fmaf(w[2], kv[2], p);
+        p = fmaf(w[3], kv[3], p);
+        const float sum = allsum32(p);  // every lane takes part in the lane moves
+        const bool act = tok && j <= mm;
+        const float t = act ? s_beta[j] * sum : 0.f;
+        if (act && (tl.lane & 31) == 0) s_coef[j * n_in + k] = rho * t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = fmaf(-t, kv[i], w[i]);
+        rho = act ? rho * s_alpha[j] : rho;
+      }
+      if (tok)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kFull || n0 + i < N) s_u[k * N + n0 + i] = rho * w[i];
     }
   }
 
   // fold: step the checkpoint through the committed entries of the full half
-  // (S <- alpha S + (beta (v - alpha S k)) k^T per entry) and write it back
+  // (S <- alpha S + (beta (v - alpha S k)) k^T per entry) and write it back.
+  // The decay is deferred: the registers hold Sh with S = 2^ls Sh, ls the sum
+  // of log2(alpha) since the last rescale, so an entry is one multiply-add per
+  // element, Sh <- Sh + beta (2^-ls v - Sh k) k^T; Sh is rescaled to S before
+  // 2^-ls passes 2^32.
   if (F > 0) {
     const T *fx = s_x + J * xs + tl.row(0);  // this lane's two consecutive rows
+    float ls = 0.f;
 #pragma unroll 1
     for (int j = 0; j < F; ++j) {
       float4 kq[4];
@@ -323,10 +355,18 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
       for (int q = 0; q < 4; ++q) kq[q] = colok(q) ? lds_ld4(s_K + j * N + tl.col(q)) : gz4();
       float xv[2];
       lds_ld_pair(fx + j * xs, xv);
-      const float al = s_falpha[j], be = s_fbeta[j];
+      const float be = s_fbeta[j];
+      ls += s_fla[j];
+      if (!(ls >= -32.f)) {  // uniform: take the decay into the registers
+        const float sc = exp2f(ls);
+#pragma unroll
+        for (int i = 0; i < R; ++i) hv[i] = fma4(sc, hv[i], 0.f, hv[i]);
+        ls = 0.f;
+      }
+      const float isig = exp2f(-ls);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        // (S k)[row]: this lane's 16 columns, then the row's eight lanes
+        // (Sh k)[row]: this lane's 16 columns, then the row's eight lanes
         float acc = hv[4 * i].x * kq[0].x;
         acc = fmaf(hv[4 * i].y, kq[0].y, acc);
         acc = fmaf(hv[4 * i].z, kq[0].z, acc);
@@ -340,10 +380,15 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
         }
         const float rd = ReplayTile::row_sum(acc);
         const float vv = (kFull || tl.row(i) < rv) ? xv[i] : 0.f;
-        const float u = be * (vv - al * rd);
+        const float u = be * fmaf(vv, isig, -rd);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hv[4 * i + q] = fma4(al, hv[4 * i + q], u, kq[q]);
+        for (int q = 0; q < 4; ++q) hv[4 * i + q] = fma4(1.f, hv[4 * i + q], u, kq[q]);
       }
+    }
+    if (ls != 0.f) {
+      const float sc = exp2f(ls);
+#pragma unroll
+      for (int i = 0; i < R; ++i) hv[i] = fma4(sc, hv[i], 0.f, hv[i]);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
