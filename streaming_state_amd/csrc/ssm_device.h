@@ -123,6 +123,9 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
 __device__ __forceinline__ float4 fma4(float s, float4 h, float u, float4 b) {
   return make_float4(s * h.x + u * b.x, s * h.y + u * b.y, s * h.z + u * b.z, s * h.w + u * b.w);
 }
+__device__ __forceinline__ float4 scale4(float4 h, float s) {
+  return make_float4(s * h.x, s * h.y, s * h.z, s * h.w);
+}
 
 // Sum eight per-row partials across the 32 lanes of a row group by recursive
 // halving: each exchange step halves the number of values a lane carries.
@@ -231,8 +234,9 @@ template <> __device__ __forceinline__ float row_totals<2>(const float v[2], int
   return s;
 }
 
-// Register tile of the verify kernels: a workgroup's four waves own 64 state
-// rows; lane l of wave w owns rows 16 w + 2 (l >> 3) + {0, 1} and, of each,
+// Register tile of the verify kernels: each wave owns 16 state rows (four
+// waves a 64-row tile, eight a 128-row one); lane l of wave w owns rows
+// 16 w + 2 (l >> 3) + {0, 1} and, of each,
 // the four 16-byte column chunks 32 q + 4 (l & 7), q = 0..3 (8 float4).  A
 // wave load instruction then reads eight whole 128-byte lines, and the total
 // of a row needs only the eight lanes of its group: one mirrored exchange
@@ -241,7 +245,7 @@ struct ReplayTile {
   int lane, wave, c, rg;
   __device__ __forceinline__ ReplayTile() {
     lane = threadIdx.x & 63;
-    wave = (threadIdx.x >> 6) & 3;
+    wave = threadIdx.x >> 6;
     c = lane & 7;
     rg = lane >> 3;
   }
@@ -344,11 +348,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // src_of(i).  Each wave instruction fills 64 consecutive chunks (lane l
 // writes 16 bytes at the wave's LDS base + 16 l; inactive lanes write
 // nothing).  The copies complete asynchronously: wait on vmcnt before use.
-template <typename SrcOf>
+template <int kWaves = kThreads / 64, typename SrcOf>
 __device__ __forceinline__ void stage_lds(char *lds, int n, SrcOf src_of) {
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  for (int blk = wave; blk * 64 < n; blk += kThreads / 64) {
+  for (int blk = wave; blk * 64 < n; blk += kWaves) {
     const int i = blk * 64 + lane;
     if (i < n)
       __builtin_amdgcn_global_load_lds(src_of(i), (lds_void_t *)(lds + blk * 1024), 16, 0, 0);

@@ -134,21 +134,25 @@ struct GdnSmem {
   }
 };
 
-// One (batch entry, head, 64-row tile) per workgroup; the state tile lives in
-// registers in the Mamba-2 verify kernel's layout (ReplayTile: two rows of
-// four 16-byte chunks per lane, eight lanes per row).  kFull: P a multiple of
-// 64 and N = 128 (no per-lane predicates); six waves per SIMD for it (at 64
-// registers the sweep and the fold spill), four for the instantiation that
-// carries the predicates.
-template <typename T, int R, bool kFull>
-__global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(ReplayArgs a,
-                                                                            ReplayMeta m,
-                                                                            LogLayout lay) {
+// One (batch entry, head, 16 kWaves-row tile) per workgroup of kWaves waves:
+// eight waves (128 rows, a whole P = 128 head) share one query sweep and one
+// copy of the key rows per head; four serve heads of fewer rows.  The state
+// tile lives in registers in the Mamba-2 verify kernel's layout (ReplayTile:
+// two rows of four 16-byte chunks per lane, eight lanes per row).  kFull: P a
+// multiple of the tile height and N = 128 (no per-lane predicates); six waves
+// per SIMD for it (at 64 registers the sweep and the fold spill), four for the
+// instantiation that carries the predicates.
+template <typename T, int R, bool kFull, int kWaves>
+__global__ __launch_bounds__(64 * kWaves, kFull ? 6 : 4) void gdn_replay_kernel(ReplayArgs a,
+                                                                               ReplayMeta m,
+                                                                               LogLayout lay) {
   extern __shared__ float4 gd_smem4[];
   char *sb = reinterpret_cast<char *>(gd_smem4);
   static_assert(R == 8, "two rows of four 16-byte chunks per lane");
+  static_assert(kWaves == 4 || kWaves == 8, "64- or 128-row tiles");
   const ReplayTile tl;
-  constexpr int kRows = 64;
+  constexpr int kRows = 16 * kWaves;
+  constexpr int kNT = 64 * kWaves;  // threads
   constexpr int E = 16 / (int)sizeof(T);  // io elements per 16-byte chunk
   constexpr int es = (int)sizeof(T);
   const Dims d = a.d;
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
     const int cx = rv / E, cv = N / E;
     const FastDiv fx(cx), fv(cv);
     auto run = [&](char *lds, const T *src, size_t stride, int rows, int chunks, FastDiv f) {
-      stage_lds(lds, rows * chunks, [&](int i) {
+      stage_lds<kWaves>(lds, rows * chunks, [&](int i) {
         const int j = f.div(i);
         return (const void *)(src + j * stride + (i - j * chunks) * E);
       });
@@ -215,13 +219,13 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
     run(sb + L.K + (F + J) * N * es, q_new, kstride, n_in, cv, fv);
   } else {  // rows not made of aligned 16-byte chunks: element copies
     const FastDiv frv(rv), fn(N);
-    for (int i = threadIdx.x; i < (J + F) * rv; i += kThreads) {
+    for (int i = threadIdx.x; i < (J + F) * rv; i += kNT) {
       const int j = frv.div(i), r = i - j * rv;
       const T *src = j >= J ? x_fold + (j - J) * xstride
                      : j < base ? x_com + j * xstride : x_new + (j - base) * xstride;
       s_x[j * xs + r] = src[r];
     }
-    for (int i = threadIdx.x; i < (F + J + n_in) * N; i += kThreads) {
+    for (int i = threadIdx.x; i < (F + J + n_in) * N; i += kNT) {
       const int r = fn.div(i), col = i - r * N;
       const T *src = r < F ? k_fold + r * kstride
                      : r < F + base ? k_com + (r - F) * kstride
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
   const T *be_com = logbeta + li.ent(slot, wh, 0) * d.H + h;
   const T *be_new = inbeta + (size_t)e * n_in * d.H + h;
   const T *be_fold = logbeta + li.ent(slot, rh, 0) * d.H + h;
-  for (int i = threadIdx.x; i < J + F; i += kThreads) {
+  for (int i = threadIdx.x; i < J + F; i += kNT) {
     if (i < J) {
       const bool com = i < base;
       const size_t o = (size_t)(com ? i : i - base) * d.H;
@@ -269,19 +273,19 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
   {
     const FastDiv frows(rv);
     T *x_app = logx + (li.ent(slot, wh, base) * d.H + h) * d.P + prow0;
-    for (int i = threadIdx.x; i < n_in * rv; i += kThreads) {
+    for (int i = threadIdx.x; i < n_in * rv; i += kNT) {
       const int k = frows.div(i), r = i - k * rv;
       x_app[k * xstride + r] = s_x[(base + k) * xs + r];
     }
     if (pt == 0)
-      for (int k = threadIdx.x; k < n_in; k += kThreads) {
+      for (int k = threadIdx.x; k < n_in; k += kNT) {
         const size_t o = li.ent(slot, wh, base + k) * d.H + h;
         logdt[o] = dt_new[(size_t)k * d.H];
         logbeta[o] = be_new[(size_t)k * d.H];
       }
     if (pt == 0 && h % hpg == 0) {
       const FastDiv fn(N);
-      for (int i = threadIdx.x; i < n_in * N; i += kThreads) {
+      for (int i = threadIdx.x; i < n_in * N; i += kNT) {
         const int k = fn.div(i), col = i - k * N;
         logk[li.ent(slot, wh, base + k) * kstride + (size_t)g * N + col] =
             s_K[(F + base + k) * N + col];
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
         for (int i = 0; i < 4; ++i) v[i] = n0 + i < N ? tofl(row[n0 + i]) : 0.f;
       }
     };
-    for (int kp = __builtin_amdgcn_readfirstlane(tl.wave); 2 * kp < n_in; kp += kThreads / 64) {
+    for (int kp = __builtin_amdgcn_readfirstlane(tl.wave); 2 * kp < n_in; kp += kWaves) {
       const int k = 2 * kp + half;
       const bool tok = k < n_in;
       const int mm = base + k;                             // this half's newest entry
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
       if (!(ls >= -32.f)) {  // uniform: take the decay into the registers
         const float sc = exp2f(ls);
 #pragma unroll
-        for (int i = 0; i < R; ++i) hv[i] = fma4(sc, hv[i], 0.f, hv[i]);
+        for (int i = 0; i < R; ++i) hv[i] = scale4(hv[i], sc);
         ls = 0.f;
       }
       const float isig = exp2f(-ls);
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
     if (ls != 0.f) {
       const float sc = exp2f(ls);
 #pragma unroll
-      for (int i = 0; i < R; ++i) hv[i] = fma4(sc, hv[i], 0.f, hv[i]);
+      for (int i = 0; i < R; ++i) hv[i] = scale4(hv[i], sc);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -420,17 +424,16 @@ __global__ __launch_bounds__(kThreads, kFull ? 6 : 4) void gdn_replay_kernel(Rep
   }
   __syncthreads();
 
-  // outputs: lane = row, one wave per in-flight token
-  static_assert(kRows == 64, "one lane per tile row");
-  if (tl.lane < rv) {
-    const int r = tl.lane;
-    T *yr = (T *)a.y + ((size_t)e * n_in * d.H + h) * d.P + prow0 + r;
-    for (int k = __builtin_amdgcn_readfirstlane(tl.wave); k < n_in; k += kThreads / 64) {
+  // outputs: one wave per (in-flight token, 64 rows of the tile), lane = row
+  constexpr int kParts = kRows / 64;
+  for (int jb = __builtin_amdgcn_readfirstlane(tl.wave); jb < n_in * kParts; jb += kWaves) {
+    const int k = jb / kParts, r = (jb % kParts) * 64 + tl.lane;
+    if (r < rv) {
       const int mm = base + k;
       float acc = s_dot[k * rv + r];
 #pragma unroll 4
       for (int j = 0; j <= mm; ++j) acc += s_coef[j * n_in + k] * tofl(s_x[j * xs + r]);
-      Io<T>::st(yr + (size_t)k * d.H * d.P, acc);
+      Io<T>::st((T *)a.y + (((size_t)e * n_in + k) * d.H + h) * d.P + prow0 + r, acc);
     }
   }
 }
@@ -449,9 +452,11 @@ hipError_t launch_gdn_copy(int io, const CopyArgs &a, const CopyMeta &m, hipStre
 
 hipError_t launch_gdn_replay(int io, const ReplayArgs &a, const ReplayMeta &m,
                              const LogLayout &lay, hipStream_t s) {
-  const int rows = 8 * kGdnR;
+  // 128-row tiles (eight waves) once a head has that many rows, else 64
+  const bool wide = a.d.P >= 128;
+  const int rows = wide ? 128 : 64;
   const int pt_n = (a.d.P + rows - 1) / rows;
-  dim3 grid(pt_n, a.d.H, a.n), block(kThreads);
+  dim3 grid(pt_n, a.d.H, a.n), block(wide ? 512 : 256);
   // xs and the row count are at most the tile height: this bounds every tile
   const size_t sm = (size_t)GdnSmem(a.W, a.n_in, a.d.N, rows, rows, io == kBF16 ? 2 : 4).total;
   const bool full = a.d.P % rows == 0 && a.d.N == 4 * 32;
@@ -461,11 +466,15 @@ hipError_t launch_gdn_replay(int io, const ReplayArgs &a, const ReplayMeta &m,
     hipLaunchKernelGGL(kernel, grid, block, sm, s, a, m, lay);
     return hipGetLastError();
   };
-  if (io == kBF16)
-    return full ? go(gdn_replay_kernel<bf16_t, kGdnR, true>)
-                : go(gdn_replay_kernel<bf16_t, kGdnR, false>);
-  return full ? go(gdn_replay_kernel<float, kGdnR, true>)
-              : go(gdn_replay_kernel<float, kGdnR, false>);
+  auto pick = [&](auto tag) {
+    using T = decltype(tag);
+    if (wide)
+      return full ? go(gdn_replay_kernel<T, kGdnR, true, 8>)
+                  : go(gdn_replay_kernel<T, kGdnR, false, 8>);
+    return full ? go(gdn_replay_kernel<T, kGdnR, true, 4>)
+                : go(gdn_replay_kernel<T, kGdnR, false, 4>);
+  };
+  return io == kBF16 ? pick(bf16_t{}) : pick(float{});
 }
 
 }  // namespace ssm

@@ -37,6 +37,9 @@ def ssm():
     (8, 5, 2, 6, 16, 1, "f32", None),       # rows not whole 16-byte chunks
     (8, 5, 2, 12, 32, 1, "bf16", None),
     (16, 5, 2, 64, 128, 1, "f32", "xoff"),  # v 4 bytes past a 16-byte boundary
+    (8, 5, 2, 200, 48, 1, "f32", None),     # 128-row tiles, the second ragged
+    (16, 5, 2, 136, 128, 1, "bf16", None),  # 128-row tiles, an 8-row second tile
+    (8, 3, 2, 130, 32, 1, "f32", None),     # 128-row tiles, rows not whole 16-byte chunks
 ])
 def test_gdn_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, var):
     S, b, steps = 6, 4, 40
