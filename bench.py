@@ -43,8 +43,8 @@ MIB = 1 << 20
 # figure into null until the counters are taken again.
 DECODE_COUNTERS = {
     "sources": ["ssm_decode.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "294efb9df64ee438ee108263de83f9cb94f6bbf1f8f827d9bc4fdf1231239146",
-    "fetch_kib": 519888.66, "write_kib": 1056769.83,
+    "sha256": "621f66d038b53276cb419095e90120d9d758a8fb2d947a36d25f9d51f82fb833",
+    "fetch_kib": 519888.57, "write_kib": 1056770.82,
     "calib_fetch_kib": 2059.01, "calib_write_kib": 4096.0, "calib_true_kib": 4096.0,
     "algorithmic_kib": 1035989.33 + 1056768.0,
 }
@@ -56,10 +56,10 @@ DECODE_COUNTERS = {
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
     "sources": ["ssm_ssd_pair.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "831d3afb3f104c030abb9f11309144ef2006b1a5f74222e4e6b9e48e2653de1a",
-    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14487844.50, "xcds": 8, "simds": 1024,
+    "sha256": "2985335372a35d3ca59b21ea3f62ca20ff2ed1507260407fef2d6bd2dde8a9d8",
+    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14229773.0, "xcds": 8, "simds": 1024,
     "mfma_mops_bf16": 722141184.0,
-    "fetch_kib": 721028.46, "write_kib": 1114112.18,
+    "fetch_kib": 721029.57, "write_kib": 1114112.31,
     # x in and y out (bf16), dt, B, C (bf16), and each sequence's final state
     # twice (into its slot and as a checkpoint)
     "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2 * 2**25,
@@ -70,8 +70,8 @@ PREFILL_COUNTERS = {
 # steps, from the log lengths, averaged).
 REPLAY_COUNTERS = {
     "sources": ["ssm_kernels.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "0c3e151d8851d3b215fc30eff4e83367146f68bea0fcdbb955f9dc8c6f790ffd",
-    "fetch_kib": 577003.95, "write_kib": 208610.13,
+    "sha256": "d751269df3d1ca1d99cee37bfc9298555699eb0ea15f7e508e31d311448b2f61",
+    "fetch_kib": 577003.33, "write_kib": 208613.47,
     "algorithmic_bytes": 1375888554.67,
 }
 

@@ -474,13 +474,18 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
       op[2 * i + k] = cat8(ld_tr(bbuf + W.bt_base[0] + ((32 * i) ^ W.bt_xor[0]) + k * 32 * kRowB),
                            ld_tr(bbuf + W.bt_base[1] + ((32 * i) ^ W.bt_xor[1]) + k * 32 * kRowB));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) W.h[i] *= lam;
-#pragma unroll
   for (int i = 0; i < 8; ++i) {
+    W.h[i] *= lam;
     pin(op[2 * i]);
     pin(op[2 * i + 1]);
 #pragma unroll
     for (int k = 0; k < 2; ++k) W.h[i] = mfma(op[2 * i + k], xt[k], W.h[i]);
+  }
+  // the decay of state tile i + 1 is issued beside tile i's products
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMA
   }
 
   // checkpoints: the post-token state of t1 - 1
