@@ -139,11 +139,12 @@ struct GdnSmem {
 // copy of the key rows per head; four serve heads of fewer rows.  The state
 // tile lives in registers in the Mamba-2 verify kernel's layout (ReplayTile:
 // two rows of four 16-byte chunks per lane, eight lanes per row).  kFull: P a
-// multiple of the tile height and N = 128 (no per-lane predicates); six waves
-// per SIMD for it (at 64 registers the sweep and the fold spill), four for the
-// instantiation that carries the predicates.
+// multiple of the tile height and N = 128 (no per-lane predicates); eight
+// waves per SIMD for it on 128-row tiles (64 registers: the fp32 fold spills
+// one, measured faster than six waves without the spill), six on 64-row
+// tiles, four for the instantiations that carry the predicates.
 template <typename T, int R, bool kFull, int kWaves>
-__global__ __launch_bounds__(64 * kWaves, kFull ? 6 : 4) void gdn_replay_kernel(ReplayArgs a,
+__global__ __launch_bounds__(64 * kWaves, kFull ? (kWaves == 8 ? 8 : 6) : 4) void gdn_replay_kernel(ReplayArgs a,
                                                                                ReplayMeta m,
                                                                                LogLayout lay) {
   extern __shared__ float4 gd_smem4[];

@@ -40,6 +40,7 @@ def ssm():
     (8, 5, 2, 200, 48, 1, "f32", None),     # 128-row tiles, the second ragged
     (16, 5, 2, 136, 128, 1, "bf16", None),  # 128-row tiles, an 8-row second tile
     (8, 3, 2, 130, 32, 1, "f32", None),     # 128-row tiles, rows not whole 16-byte chunks
+    (16, 5, 2, 128, 128, 1, "f32", "strong"),  # dt x 25: gates down to e^-50 and below
 ])
 def test_gdn_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, var):
     S, b, steps = 6, 4, 40
@@ -61,6 +62,8 @@ def test_gdn_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, var):
     sched = oracle.replay_schedule(acc, W, n_in)
     for s in range(steps):
         v, dt, beta, k, q = inputs.gdn_tokens(45, b * n_in, H, P, N, G, s)
+        if var == "strong":  # products of gates that underflow fp32 within a window
+            dt = dt * np.float32(25.0)
         arrs = [v.reshape(b, n_in, H, P), dt.reshape(b, n_in, H), beta.reshape(b, n_in, H),
                 k.reshape(b, n_in, G, N), q.reshape(b, n_in, G, N)]
         if io == "bf16":
