@@ -159,7 +159,14 @@ __global__ __launch_bounds__(64 * kWaves, kFull ? (kWaves == 8 ? 8 : 6) : 4) voi
   const Dims d = a.d;
   const int W = a.W, n_in = a.n_in;
   const int N = kFull ? 4 * 32 : d.N;
-  const int pt = blockIdx.x, h = blockIdx.y, e = blockIdx.z;
+  const int pt = blockIdx.x, e = blockIdx.z;
+  // Two value heads per key group (H a multiple of 16): the heads of group g
+  // are placed eight workgroup slots apart, so that the round-robin dispatch
+  // over the eight XCDs puts both on one XCD and the second one's key rows are
+  // hits in that XCD's L2.  Otherwise heads in order.
+  const int h = (d.H == 2 * d.G && d.H % 16 == 0)
+                    ? (blockIdx.y & ~15) + 2 * (blockIdx.y & 7) + ((blockIdx.y >> 3) & 1)
+                    : (int)blockIdx.y;
   const int slot = m.slot[e];
   const uint32_t info = m.info[e];
   const int F = info_fold(info);
