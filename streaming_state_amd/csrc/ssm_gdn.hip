@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void gdn_copy_kernel(CopyArgs a, CopyMeta
 // ===========================================================================
 // ReplaySSM verify
 // ===========================================================================
-constexpr int kGdnR = 8;  // 64-row tiles
+constexpr int kGdnR = 8;  // float4 per lane: two state rows of four 16-byte chunks
 
 // LDS carve-up (byte offsets; W window, n_in in-flight tokens, xs the LDS stride
 // of an entry's v rows, rows the tile's row count, es the io element size).
@@ -115,18 +115,18 @@ constexpr int kGdnR = 8;  // 64-row tiles
 // folds none (J <= W), so key rows never exceed W + 2 n_in and v rows W + n_in.
 //   K [W + 2 n_in][N] io   fold k rows, then combined k rows, then in-flight q
 //   x [W + n_in][xs] io    combined v rows, then fold v rows
-//   alpha, beta [W] (combined), falpha, fbeta [W] (fold), coef [W][n_in],
+//   alpha, beta [W] (combined), fla = log2(alpha), fbeta [W] (fold), coef [W][n_in],
 //   u [n_in][N], dot [n_in][rows]   (fp32)
 struct GdnSmem {
-  int K, x, alpha, beta, falpha, fbeta, coef, u, dot, total;
+  int K, x, alpha, beta, fla, fbeta, coef, u, dot, total;
   __host__ __device__ GdnSmem(int W, int n_in, int N, int xs, int rows, int es) {
     auto up16 = [](int b) { return (b + 15) & ~15; };
     K = 0;
     x = up16(K + (W + 2 * n_in) * N * es);
     alpha = up16(x + (W + n_in) * xs * es);
     beta = alpha + 4 * W;
-    falpha = beta + 4 * W;
-    fbeta = falpha + 4 * W;
+    fla = beta + 4 * W;
+    fbeta = fla + 4 * W;
     coef = fbeta + 4 * W;
     u = up16(coef + 4 * W * n_in);
     dot = u + 4 * n_in * N;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * kWaves, kFull ? (kWaves == 8 ? 8 : 6) : 4) voi
   T *s_K = (T *)(sb + L.K);
   T *s_x = (T *)(sb + L.x);
   float *s_alpha = (float *)(sb + L.alpha), *s_beta = (float *)(sb + L.beta);
-  float *s_fla = (float *)(sb + L.falpha), *s_fbeta = (float *)(sb + L.fbeta);
+  float *s_fla = (float *)(sb + L.fla), *s_fbeta = (float *)(sb + L.fbeta);
   float *s_coef = (float *)(sb + L.coef), *s_u = (float *)(sb + L.u);
   float *s_dot = (float *)(sb + L.dot);
 
