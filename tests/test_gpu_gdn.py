@@ -43,6 +43,8 @@ def ssm():
     (16, 5, 2, 128, 128, 1, "f32", "strong"),  # dt x 25: gates down to e^-50 and below
     (64, 16, 2, 128, 128, 1, "f32", None),  # 128-row tile at the largest window and in-flight count
     (8, 5, 4, 256, 64, 2, "bf16", None),    # two 128-row tiles per head, two key groups
+    (8, 5, 16, 64, 128, 8, "f32", None),    # two value heads per group, 16 heads (XCD-paired order)
+    (16, 5, 32, 128, 64, 16, "f32", None),  # the same with 128-row tiles
 ])
 def test_gdn_replay_and_copy_vs_oracle(ssm, W, n_in, H, P, N, G, io, var):
     S, b, steps = 6, 4, 40
