@@ -59,7 +59,8 @@ constexpr int SN = 128;  // state size
 
 // LDS map (bytes).  C, B and X (x of both heads, [t][2P]) are double-buffered
 // 64-row tiles of 256-byte rows; M holds one 64 x 64 bf16 matrix per head;
-// each wave has a private area for its running sums.
+// each head has an area for its running sums, written by one wave and read by
+// all eight.
 constexpr int kRowB = 256;
 constexpr int kTileB = Q * kRowB;
 constexpr int kOffC = 0;
@@ -68,8 +69,11 @@ constexpr int kOffX = 4 * kTileB;
 constexpr int kOffM = 6 * kTileB;
 constexpr int kMHeadB = Q * Q * 2;
 constexpr int kOffSums = kOffM + 2 * kMHeadB;
-constexpr int kSumsB = 6 * Q * 4;  // cs of both heads, cs - log2(dt) of both, exp(cs), w
-constexpr int kOffDt = kOffSums + 8 * kSumsB;  // dt of both heads per token, per buffer
+// running sums of one head: rows cs, cs - log2|dt|, exp(cs), w (64 floats
+// each), then exp(cs_end) and a negative-dt flag
+constexpr int kSumsB = 4 * Q * 4 + 16;
+constexpr int kSumLam = 4 * Q * 4, kSumNeg = kSumLam + 4;
+constexpr int kOffDt = kOffSums + 2 * kSumsB;  // dt of both heads per token, per buffer
 constexpr int kSmemB = kOffDt + 2 * Q * 4;
 static_assert(kSmemB <= 160 * 1024, "fits the LDS of one CU");
 
@@ -193,14 +197,13 @@ struct Wave {
   int o_x[2];    // x, transposing, rows +0 / +4
   int bt_base[2], bt_xor[2];  // B^T, transposing, rows +0 / +4: n tile i at base + (32 i ^ xor)
   int o_m[2];    // M rows for G2, per K step
-  int sums;      // this wave's running-sum area
+  int sums;      // this wave's head's running-sum area
   // staging: per-lane source offsets of full blocks (row 8w + 4u + g)
   uint32_t v_b[2], v_x[2], v_c[2];
   // state and output accumulators
   f32x4_t h[8];  // h^T[n = 16i + 4g + r][p = 16 ps + li]
   f32x4_t y[4];  // y^T[p = 16 ps + 4g + r][t = 16 tt + li]
   bool have_h;
-  float lam;     // exp(cs_end) of the current block, own head
   bool neg;      // some dt of the current block is negative (either head)
   bool stores4;  // exactly four global stores followed the last input loads
 };
@@ -290,8 +293,8 @@ __device__ __forceinline__ Tile tile_load(const Wave &W, int id, int bbuf, int c
   }
 #pragma unroll
   for (int hq = 0; hq < 2; ++hq) {
-    t.cst[hq] = ld_lds<float>(W.sums + hq * 256 + 4 * (16 * t.b + W.li));
-    t.cp[hq] = ld_lds<f32x4_t>(W.sums + (2 + hq) * 256 + 4 * (16 * t.a + 4 * W.g));
+    t.cst[hq] = ld_lds<float>(kOffSums + hq * kSumsB + 4 * (16 * t.b + W.li));
+    t.cp[hq] = ld_lds<f32x4_t>(kOffSums + hq * kSumsB + 256 + 4 * (16 * t.a + 4 * W.g));
   }
   return t;
 }
@@ -335,31 +338,32 @@ __device__ __forceinline__ void tile_mask(const Wave &W, const Seg &S, Tile &t, 
   }
 }
 
-// Running sums of dt*A (log2 units) of a block, one token per lane, both heads,
-// into this wave's area: cs of both heads, cs - log2|dt| of both (the mask's
-// exp2(cs_t - this) carries the |dt_s| factor; dt = 0, past the block end,
-// gives +inf and a zero weight), exp(cs) and the G3 weights of its own head.
-// Sets W.neg when a dt of the block is negative; returns exp(cs_end) of its
-// own head.
-__device__ __forceinline__ float block_sums(Wave &W, const Seg &S, int buf, int len) {
+// Running sums of dt*A (log2 units) of a block for head hq, one token per
+// lane, into the head's area: cs, cs - log2|dt| (the mask's exp2(cs_t - this)
+// carries the |dt_s| factor; dt = 0, past the block end, gives +inf and a zero
+// weight), exp(cs), the G3 weights, exp(cs_end) and whether a dt of the block
+// is negative.  One wave per head (on different SIMDs) computes them; the
+// barrier that opens the block makes them visible to the other seven.
+__device__ __forceinline__ void block_sums(const Wave &W, const Seg &S, int buf, int len, int hq) {
   const int lane = W.lane;
   const uint32_t dtw = ld_lds<uint32_t>(kOffDt + buf * Q * 4 + 4 * lane);
-  const float dq0 = lane < len ? __uint_as_float(dtw << 16) : 0.f;
-  const float dq1 = lane < len ? __uint_as_float(dtw & 0xffff0000u) : 0.f;
-  const float c0 = scan64(dq0 * S.al2[0]);
-  const float c1 = scan64(dq1 * S.al2[1]);
-  const float cq = W.q ? c1 : c0, dqq = W.q ? dq1 : dq0;
-  const float endq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cq), 63));
-  const int s = W.sums + 4 * lane;
-  st_lds<float>(s + 0 * 256, c0);
-  st_lds<float>(s + 1 * 256, c1);
-  st_lds<float>(s + 2 * 256, c0 - __builtin_amdgcn_logf(fabsf(dq0)));
-  st_lds<float>(s + 3 * 256, c1 - __builtin_amdgcn_logf(fabsf(dq1)));
-  W.neg = __builtin_amdgcn_ballot_w64(dq0 < 0.f || dq1 < 0.f) != 0;
-  st_lds<float>(s + 4 * 256, __builtin_amdgcn_exp2f(cq));
-  st_lds<float>(s + 5 * 256, __builtin_amdgcn_exp2f(endq - cq) * dqq);
-  return __builtin_amdgcn_exp2f(endq);
+  const float dq = lane < len ? __uint_as_float(hq ? (dtw & 0xffff0000u) : (dtw << 16)) : 0.f;
+  const float c = scan64(dq * (hq ? S.al2[1] : S.al2[0]));
+  const float end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+  const int area = kOffSums + hq * kSumsB;
+  const int s = area + 4 * lane;
+  st_lds<float>(s + 0 * 256, c);
+  st_lds<float>(s + 1 * 256, c - __builtin_amdgcn_logf(fabsf(dq)));
+  st_lds<float>(s + 2 * 256, __builtin_amdgcn_exp2f(c));
+  st_lds<float>(s + 3 * 256, __builtin_amdgcn_exp2f(end - c) * dq);
+  const bool neg = __builtin_amdgcn_ballot_w64(dq < 0.f) != 0;
+  if (lane == 0) {
+    st_lds<float>(area + kSumLam, __builtin_amdgcn_exp2f(end));
+    st_lds<uint32_t>(area + kSumNeg, neg ? 1u : 0u);
+  }
 }
+// the wave that computes head hq's sums: waves 0 and 5 (SIMDs 0 and 1)
+__device__ __forceinline__ bool sums_wave(const Wave &W) { return W.w == 0 || W.w == 5; }
 
 template <int BUF>
 __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m, Wave &W, Seg &S) {
@@ -379,7 +383,9 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
   else
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();  // [A] inputs of this block visible; the other buffer is free
-  const float lam = W.lam;  // this block's sums were written during the previous one
+  // this block's sums were written during the previous one
+  const float lam = ld_lds<float>(W.sums + kSumLam);
+  W.neg = (ld_lds<uint32_t>(kOffSums + kSumNeg) | ld_lds<uint32_t>(kOffSums + kSumsB + kSumNeg)) != 0;
   const Loads nl = prepare_loads(a, W, S, BUF ^ 1, S.n0, S.n1 - S.n0);
 
   const int li = W.li, g = W.g, q = W.q;
@@ -406,10 +412,10 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
   for (int k = 0; k < 2; ++k)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      wv[2 * k + e] = ld_lds<f32x4_t>(W.sums + 5 * 256 + 4 * (32 * k + 8 * g + 4 * e));
+      wv[2 * k + e] = ld_lds<f32x4_t>(W.sums + 3 * 256 + 4 * (32 * k + 8 * g + 4 * e));
   float ev[4];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) ev[tt] = ld_lds<float>(W.sums + 4 * 256 + 4 * (16 * tt + li));
+  for (int tt = 0; tt < 4; ++tt) ev[tt] = ld_lds<float>(W.sums + 2 * 256 + 4 * (16 * tt + li));
   if (more) issue_part(nl, W, 0, BUF ^ 1);
 
   // ---- G4: y^T[p,t] = exp(cs_t) sum_n h_prev[p,n] C[t,n]
@@ -512,7 +518,7 @@ __device__ __forceinline__ bool pair_block(const ScanArgs &a, const ScanMeta &m,
 #pragma unroll
   for (int tt = 2; tt < 4; ++tt) mo[2 + tt] = ld_lds<bf16x8_t>(mb + tt * 16 * 128 + W.o_m[1]);
   // the next block's sums, while M is read (this block's were last read by G3)
-  if (more) W.lam = block_sums(W, S, BUF ^ 1, S.n1 - S.n0);
+  if (more && sums_wave(W)) block_sums(W, S, BUF ^ 1, S.n1 - S.n0, W.q);
 #pragma unroll
   for (int i = 0; i < 6; ++i) pin(mo[i]);
 #pragma unroll
@@ -575,7 +581,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void scan_ssd_pair_kernel(ScanArgs
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) W.o_m[k] = m_off(li, 4 * k + g);
-  W.sums = kOffSums + W.w * kSumsB;
+  W.sums = kOffSums + W.q * kSumsB;
   {
     const size_t sCB = (size_t)d.G * SN * 2, sX = (size_t)d.H * SP * 2;
 #pragma unroll
@@ -624,7 +630,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void scan_ssd_pair_kernel(ScanArgs
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  W.lam = block_sums(W, S, 0, S.t1 - S.t0);
+  if (sums_wave(W)) block_sums(W, S, 0, S.t1 - S.t0, W.q);
   W.stores4 = false;
 
   while (pair_block<0>(a, m, W, S) && pair_block<1>(a, m, W, S)) {
