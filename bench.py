@@ -56,10 +56,10 @@ DECODE_COUNTERS = {
 # HBM counters with the copy calibration above.
 PREFILL_COUNTERS = {
     "sources": ["ssm_ssd_pair.hip", "ssm_device.h", "ssm_internal.h"],
-    "sha256": "2985335372a35d3ca59b21ea3f62ca20ff2ed1507260407fef2d6bd2dde8a9d8",
-    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 14229773.0, "xcds": 8, "simds": 1024,
+    "sha256": "832afb19a52f45ded11133edf7e26b117602a38b8376c7a08f3164a611369340",
+    "mfma_busy_cycles": 361070592.0, "gui_active_cycles": 13773072.5, "xcds": 8, "simds": 1024,
     "mfma_mops_bf16": 722141184.0,
-    "fetch_kib": 721029.57, "write_kib": 1114112.31,
+    "fetch_kib": 721082.55, "write_kib": 1114124.34,
     # x in and y out (bf16), dt, B, C (bf16), and each sequence's final state
     # twice (into its slot and as a checkpoint)
     "algorithmic_bytes": 2 * 2**30 + 3 * 2**24 + 2 * 2**25,
